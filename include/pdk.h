@@ -1,0 +1,318 @@
+/*
+ * pdk.h - paged split-KV decode attention for MI355X (gfx950): C ABI.
+ *
+ * Sources, cited by page title and section:
+ *   [cascade-PR]  mlxcel pull request "perf(core): compute shared prompt
+ *                 prefixes once per decode batch".
+ *   [DCP-PR]      ROCm/ATOM pull request "[feat][DCP] Optimize MLA DCP
+ *                 (Enable Prefix Cache / Chunked Prefill + FP8 KVCache)".
+ *   [OCP-FP8]     OCP 8-bit floating point specification (E4M3).
+ *
+ * Conventions for every entry point:
+ *   - Return value is a pdk_status; PDK_OK (0) on success. Nothing aborts or
+ *     throws across this boundary. pdk_last_error() returns a thread-local
+ *     message describing the last non-OK status on the calling thread.
+ *   - GPU work is enqueued asynchronously on the given hipStream_t (0 = the
+ *     null stream). No entry point allocates device memory: the caller owns
+ *     every buffer, and workspaces are sized by the *_workspace_bytes queries.
+ *   - Pointers named *_dev or documented "device" are device pointers; all
+ *     others are host pointers. Device pointers are borrowed for the call
+ *     (and until the enqueued work has finished); the library keeps none.
+ *   - State tensors: partial and merged outputs are float32, normalized by
+ *     their own softmax denominator; LSEs are float32 in log2 units,
+ *     lse = m + log2(l) where m is the running max of the log2-scaled scores
+ *     and l the sum of 2^(s - m) [cascade-PR, "How the #898 merge kernel is
+ *     reused"]. An empty key range yields out = 0, lse = -inf.
+ *   - KV pools are HND: [num_blocks, num_kv_heads, page_size, head_dim], row
+ *     major. A latent pool (MLA) has one KV head, v == NULL and
+ *     head_dim_v <= head_dim_k: the value of a token is the first head_dim_v
+ *     lanes of its key row [DCP-PR, 3.2: the compressed latent serves as both].
+ *   - Page table: CSR indptr[batch+1], indices[indptr[batch]] (pool rows),
+ *     kv_len[batch] (tokens). Token t of request b lives in slot t % P of row
+ *     indices[indptr[b] + t / P]; indptr[b+1] - indptr[b] == ceil(kv_len[b]/P).
+ *     Kernels never read a row outside [0, num_blocks) nor a token at or past
+ *     kv_len[b]; a malformed device CSR gives wrong numbers but no fault.
+ *     pdk_validate_csr checks a host copy.
+ *   - Query: one token per request, q [batch, num_q_heads, head_dim_k] in f32
+ *     or bf16, row major. Query head i reads KV head i / (Hq / Hkv)
+ *     [cascade-PR, "The decomposition, and the one part that is not obvious"].
+ */
+#ifndef PDK_H
+#define PDK_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PDK_F32 = 0, PDK_BF16 = 1, PDK_FP8_E4M3 = 2 } pdk_dtype;
+
+typedef enum {
+  PDK_OK = 0,
+  PDK_ERR_ARG = -1,          /* null pointer or out-of-range scalar */
+  PDK_ERR_SHAPE = -2,        /* inconsistent sizes or page table */
+  PDK_ERR_DTYPE = -3,        /* dtype not accepted by this entry point */
+  PDK_ERR_UNSUPPORTED = -4,  /* valid, but no kernel instantiated for it */
+  PDK_ERR_WORKSPACE = -5,    /* workspace too small or plan not uploaded */
+  PDK_ERR_HIP = -6           /* a HIP runtime call failed */
+} pdk_status;
+
+/* Why a cascade plan fell back to the flat launch [cascade-PR, "Task items"
+ * item 4, and "Proving which path a benchmark arm took"]. */
+typedef enum {
+  PDK_DECLINE_NONE = 0,
+  PDK_DECLINE_DISABLED = 1,
+  PDK_DECLINE_NO_CANDIDATE = 2,
+  PDK_DECLINE_MEMBERS_BELOW_MIN = 3,
+  PDK_DECLINE_SPAN_BELOW_MIN = 4,
+  PDK_DECLINE_REACHES_LAST_PAGE = 5
+} pdk_decline;
+
+typedef struct {
+  const void* k;          /* device, HND [num_blocks, Hkv, P, head_dim_k] */
+  const void* v;          /* device, HND [num_blocks, Hkv, P, head_dim_v]; NULL: latent pool */
+  int32_t num_blocks;
+  int32_t page_size;      /* P, tokens per page */
+  int32_t num_kv_heads;   /* Hkv */
+  int32_t head_dim_k;
+  int32_t head_dim_v;
+  int32_t dtype;          /* pdk_dtype of k and v */
+  float k_scale;          /* fp8 only: per-tensor dequant scale of k */
+  float v_scale;          /* fp8 only: per-tensor dequant scale of v (latent: unused) */
+} pdk_kv_pool;
+
+typedef struct {
+  const int32_t* indptr;  /* [batch + 1] */
+  const int32_t* indices; /* [nnz] */
+  const int32_t* kv_len;  /* [batch] */
+  int32_t batch;
+  int32_t nnz;            /* indptr[batch] */
+} pdk_csr;
+
+/* ---------------------------------------------------------------------- */
+/* Host-side integer work                                                 */
+/* ---------------------------------------------------------------------- */
+
+/* Split-KV partitions [cascade-PR, "Test plan": cross-CTA split-KV with a
+ * heuristic chunk size]: partitions tile each request's range from its first
+ * token in partition_tokens steps, the last one short.
+ * part_indptr[b+1] = part_indptr[b] + ceil(kv_len[b] / partition_tokens).
+ * Host arrays: kv_len [batch] in, part_indptr [batch+1] out.
+ * Errors: PDK_ERR_ARG (null, batch < 0, partition_tokens <= 0, kv_len < 0). */
+int pdk_partition_indptr(const int32_t* kv_len, int32_t batch, int32_t partition_tokens,
+                         int32_t* part_indptr);
+
+/* Checks a host copy of a page table: indptr[0] == 0, monotone,
+ * indptr[batch] == nnz, page counts == ceil(kv_len/P), ids in [0, num_blocks).
+ * Returns PDK_OK or PDK_ERR_SHAPE with the first violation in pdk_last_error. */
+int pdk_validate_csr(const pdk_csr* csr, int32_t page_size, int32_t num_blocks);
+
+/* Kill-switch parse [cascade-PR, "Task items" item 4]: after trimming blanks
+ * and ignoring case, 0/false/off/no -> 0 and 1/true/on/yes -> 1; anything
+ * else, or NULL, -> -1 (the shipped default, which is off).
+ * pdk_cascade_enabled_from_env reads the named environment variable. */
+int pdk_parse_switch(const char* value);
+int pdk_cascade_enabled_from_env(const char* var_name);
+
+/* KV-head-major stacking [cascade-PR, "The decomposition"]: for every stacked
+ * head h0 = kv*(M*G) + m*G + g, out[h0] = m*Hq + (kv*G + g), Hq = Hkv*G.
+ * Host array out [M*Hq]. */
+int pdk_stacked_head_map(int32_t num_members, int32_t num_kv_heads, int32_t group,
+                         int32_t* out);
+
+/* ---------------------------------------------------------------------- */
+/* GPU kernels                                                            */
+/* ---------------------------------------------------------------------- */
+
+/* One normalized partial state per (request, partition, query head)
+ * [cascade-PR, "The decomposition": one workgroup owns every query head of
+ * one KV head for one (request, page tile) and loads each K/V element once].
+ * csr_dev: device page table; part_indptr_dev: device [batch+1] from
+ * pdk_partition_indptr; num_partitions = part_indptr[batch].
+ * Outputs v_part [num_partitions, num_q_heads, head_dim_v] and
+ * lse_part [num_partitions, num_q_heads], row = part_indptr[b] + p.
+ * partition_tokens must be a positive multiple of page_size.
+ * Dtypes: q f32|bf16; pool f32|bf16|fp8_e4m3 (fp8 is dequantized to bf16
+ * with the pool's scale on load [DCP-PR, 3.2 figure, 3.3]).
+ * Errors: PDK_ERR_ARG, PDK_ERR_SHAPE, PDK_ERR_DTYPE, PDK_ERR_UNSUPPORTED
+ * (head dims / head counts without an instantiated kernel), PDK_ERR_HIP. */
+int pdk_paged_decode_partial(const pdk_kv_pool* pool, const pdk_csr* csr_dev, const void* q,
+                             int32_t q_dtype, int32_t num_q_heads, float sm_scale,
+                             int32_t partition_tokens, const int32_t* part_indptr_dev,
+                             int32_t num_partitions, float* v_part, float* lse_part,
+                             hipStream_t stream);
+
+/* Merge of states [cascade-PR, "How the #898 merge kernel is reused"]:
+ * output row j combines input rows o_indptr[j] <= r < o_indptr[j+1]:
+ * m = max lse_r, w_r = 2^(lse_r - m), l = sum w_r, v_out = sum w_r v_r / l,
+ * lse_out = m + log2 l. Rows with lse = -inf are skipped; an empty group or
+ * one with only -inf rows gives (0, -inf); a group of one row is copied
+ * bit for bit (the identity the page relies on).
+ * Device arrays: v_in [num_in, H, D], lse_in [num_in, H], o_indptr [num_out + 1],
+ * v_out [num_out, H, D], lse_out [num_out, H] (may be NULL). Group bounds are
+ * clamped to [0, num_in) on the device, so a bad o_indptr never reads past
+ * the inputs. D must be a multiple of 4.
+ * Errors: PDK_ERR_ARG, PDK_ERR_SHAPE, PDK_ERR_HIP. */
+int pdk_merge_states(const float* v_in, const float* lse_in, int32_t num_in,
+                     const int32_t* o_indptr_dev, int32_t num_out, int32_t num_heads,
+                     int32_t head_dim, float* v_out, float* lse_out, hipStream_t stream);
+
+/* Flat split-KV decode = pdk_paged_decode_partial + pdk_merge_states
+ * [cascade-PR, "How the #898 merge kernel is reused": launch_with_lse returns
+ * the (V, LSE) pair]. out [batch, Hq, head_dim_v], lse_out [batch, Hq]
+ * (may be NULL). workspace: device, at least
+ * pdk_decode_flat_workspace_bytes(num_partitions, Hq, head_dim_v) bytes. */
+size_t pdk_decode_flat_workspace_bytes(int32_t num_partitions, int32_t num_q_heads,
+                                       int32_t head_dim_v);
+int pdk_decode_flat(const pdk_kv_pool* pool, const pdk_csr* csr_dev, const void* q,
+                    int32_t q_dtype, int32_t num_q_heads, float sm_scale,
+                    int32_t partition_tokens, const int32_t* part_indptr_dev,
+                    int32_t num_partitions, float* out, float* lse_out, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream);
+
+/* Stack the query heads of M members KV-head-major, [M, Hkv, G, D] ->
+ * [Hkv, M, G, D] [cascade-PR, "The decomposition"]: q0[h0] = q[members[m],
+ * kv*G + g] for h0 = kv*(M*G) + m*G + g. q [*, Hkv*G, D] (f32|bf16),
+ * members_dev [M], q0 [M*Hkv*G, D] in q's dtype. */
+int pdk_stack_heads(const void* q, int32_t q_dtype, const int32_t* members_dev,
+                    int32_t num_members, int32_t num_kv_heads, int32_t group, int32_t head_dim,
+                    void* q0, hipStream_t stream);
+
+/* The inverse on states: out[m, kv*G + g] = in0[kv*(M*G) + m*G + g] for
+ * v [M*Hq, D] -> [M, Hq, D] and lse [M*Hq] -> [M, Hq] (lse pointers may both
+ * be NULL). f32 device arrays. */
+int pdk_unstack_heads(const float* v0, const float* lse0, int32_t num_members,
+                      int32_t num_kv_heads, int32_t group, int32_t head_dim, float* v_out,
+                      float* lse_out, hipStream_t stream);
+
+/* fp8 E4M3FN -> bf16 with a per-tensor scale, exactly as the attention
+ * kernels dequantize on load [DCP-PR, 3.2 figure]: bf16 = RNE_bf16(f32(x) *
+ * scale) with the product rounded to nearest even in binary32 [OCP-FP8].
+ * Device arrays in [n] (uint8), out [n] (bf16 bit patterns). */
+int pdk_fp8_dequant_bf16(const uint8_t* in, int64_t n, float scale, uint16_t* out,
+                         hipStream_t stream);
+
+/* ---------------------------------------------------------------------- */
+/* Cascade (shared-prefix) decode [cascade-PR, "Task items" items 1-4]     */
+/* ---------------------------------------------------------------------- */
+
+typedef struct {
+  int32_t enabled;             /* -1: shipped default (off); 0: off; 1: on */
+  int32_t min_shared_pages;    /* span threshold in pages (default 16), >= 1 */
+  int32_t min_members;         /* member threshold (default 2), >= 2 */
+  int32_t max_groups;          /* 1: the page's single subgroup (default);
+                                  0: every qualifying group; k: the best k */
+  int32_t l0_partition_tokens; /* level-0 partition size, multiple of P */
+  int32_t l1_partition_tokens; /* level-1 (and flat) partition size, multiple of P */
+} pdk_cascade_params;
+
+void pdk_cascade_params_default(pdk_cascade_params* params);
+
+typedef struct pdk_cascade_plan pdk_cascade_plan;
+
+/* Detect shared prefixes in a HOST page table and build the two-level plan
+ * [cascade-PR, "Detection reads the page table, not the refcounts", "Task
+ * items" 1, 2, 4]. Grouping by first page, positional longest common page
+ * prefix capped to full pages, rejection of spans that reach a member's last
+ * page or fall below the thresholds, selection by span*(members-1), ties to
+ * the lowest first batch index. A declined plan is not an error: it returns
+ * PDK_OK with a decline reason and runs the flat path. The plan is owned by
+ * the library until pdk_cascade_plan_free. page_size must match the pool. */
+int pdk_cascade_plan_create(const pdk_csr* csr_host, int32_t page_size,
+                            const pdk_cascade_params* params, pdk_cascade_plan** plan_out);
+void pdk_cascade_plan_free(pdk_cascade_plan* plan);
+
+/* Read-only views of the plan's host arrays (valid until the plan is freed). */
+enum {
+  PDK_PLAN_MEMBERS = 0,         /* [total members] batch indices, level-0 order */
+  PDK_PLAN_GROUP_INDPTR = 1,    /* [K+1] offsets of each group into MEMBERS */
+  PDK_PLAN_SPAN_PAGES = 2,      /* [K] */
+  PDK_PLAN_L0_INDPTR = 3,       /* [K+1] level-0 view */
+  PDK_PLAN_L0_INDICES = 4,
+  PDK_PLAN_L0_LEN = 5,          /* [K] tokens */
+  PDK_PLAN_L1_INDPTR = 6,       /* [B+1] level-1 view (= flat view when declined) */
+  PDK_PLAN_L1_INDICES = 7,
+  PDK_PLAN_L1_LEN = 8,          /* [B] */
+  PDK_PLAN_MERGE_INDPTR = 9,    /* [B+1] the page's pairing: 2 rows per member, else 1 */
+  PDK_PLAN_FUSED_MERGE_INDPTR = 10, /* [B+1] rows per request in the single merge */
+  PDK_PLAN_GROUP_OF = 11,       /* [B] level-0 group of each request, -1 if none */
+  PDK_PLAN_MEMBER_RANK = 12,    /* [B] rank within its group, -1 if none */
+  PDK_PLAN_NUM_FIELDS = 13
+};
+int pdk_cascade_plan_get(const pdk_cascade_plan* plan, int32_t field, const int32_t** data,
+                         int32_t* len);
+
+/* stats = {batch, members, shared_pages, shared_tokens, prefix_chunks,
+ * suffix_chunks} [cascade-PR, "Proving which path a benchmark arm took"];
+ * decline receives a pdk_decline. Either pointer may be NULL. */
+int pdk_cascade_plan_stats(const pdk_cascade_plan* plan, int32_t stats[6], int32_t* decline);
+
+/* Device workspace for pdk_run_cascade_decode: the plan's integer arrays
+ * followed by the partial states of both levels. */
+size_t pdk_cascade_workspace_bytes(const pdk_cascade_plan* plan, int32_t num_q_heads,
+                                   int32_t head_dim_v);
+
+/* Copy the plan's integer arrays into the head of the workspace
+ * (hipMemcpyAsync on stream). The plan must stay alive until the copy has
+ * completed. Must precede pdk_run_cascade_decode with the same workspace. */
+int pdk_cascade_plan_upload(pdk_cascade_plan* plan, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/* Run the plan [cascade-PR, "Task items" item 2]: one level-0 launch over
+ * each selected group's span with the members' query heads stacked
+ * KV-head-major (partials written straight into the members' rows), one
+ * level-1 launch over every request's remaining range, then one merge per
+ * request over [level-0 partitions][level-1 partitions] - equal to the
+ * page's level merge followed by the pair merge, by associativity. A
+ * declined plan runs the flat path. out [B, Hq, head_dim_v], lse_out [B, Hq]
+ * (may be NULL). */
+int pdk_run_cascade_decode(const pdk_cascade_plan* plan, const pdk_kv_pool* pool, const void* q,
+                           int32_t q_dtype, int32_t num_q_heads, float sm_scale, float* out,
+                           float* lse_out, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/* ---------------------------------------------------------------------- */
+/* Chunked cached prefix + new suffix (one GPU's share of MLA decode)      */
+/* [DCP-PR, 3.2 figure]                                                    */
+/* ---------------------------------------------------------------------- */
+
+typedef struct pdk_chunked_plan pdk_chunked_plan;
+
+/* Host-side split of each request's cached range into chunks of
+ * chunk_tokens (aligned at token 0), each chunk into partitions of
+ * partition_tokens; plus the suffix partitions. Both page tables are HOST
+ * copies; chunk_tokens and partition sizes are multiples of their page sizes. */
+int pdk_chunked_plan_create(const pdk_csr* prefix_host, int32_t prefix_page_size,
+                            int32_t chunk_tokens, int32_t prefix_partition_tokens,
+                            const pdk_csr* suffix_host, int32_t suffix_page_size,
+                            int32_t suffix_partition_tokens, pdk_chunked_plan** plan_out);
+void pdk_chunked_plan_free(pdk_chunked_plan* plan);
+/* counts = {batch, chunks, prefix_partitions, suffix_partitions} */
+int pdk_chunked_plan_counts(const pdk_chunked_plan* plan, int32_t counts[4]);
+size_t pdk_chunked_workspace_bytes(const pdk_chunked_plan* plan, int32_t num_q_heads,
+                                   int32_t head_dim_v);
+int pdk_chunked_plan_upload(pdk_chunked_plan* plan, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/* Chunk partials -> merge per chunk (chunk_out/chunk_lse, each chunk's
+ * (O, LSE)) -> merge across each request's chunks -> suffix partials and
+ * merge -> merge of the prefix state with the suffix state. chunk_out
+ * [chunks, Hq, Dv] and chunk_lse [chunks, Hq] are caller buffers (may be NULL
+ * to keep them inside the workspace). out [B, Hq, Dv], lse_out [B, Hq]. */
+int pdk_run_chunked_decode(const pdk_chunked_plan* plan, const pdk_kv_pool* prefix_pool,
+                           const pdk_kv_pool* suffix_pool, const void* q, int32_t q_dtype,
+                           int32_t num_q_heads, float sm_scale, float* out, float* lse_out,
+                           float* chunk_out, float* chunk_lse, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/* Thread-local description of the last non-OK status on this thread. */
+const char* pdk_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PDK_H */

@@ -1,0 +1,464 @@
+"""Paged split-KV decode attention for MI355X (gfx950): Python binding.
+
+A thin ctypes layer over the C ABI of ``libpdk.so`` (declared in
+``include/pdk.h``). It only marshals arguments: every step of the decode
+path (partials, merges, head stacking, fp8 dequant) runs in the library's
+HIP kernels, and the planner runs in its C++ host code. PyTorch is used for
+device memory and the current HIP stream. There is no CPU fallback: if the
+library is missing or fails to load, every call raises.
+
+Sources: mlxcel pull request "perf(core): compute shared prompt prefixes once
+per decode batch" (cascade decode, merge_states contract) and ROCm/ATOM pull
+request "[feat][DCP] Optimize MLA DCP (Enable Prefix Cache / Chunked Prefill
++ FP8 KVCache)" (chunked cached prefix, fp8 dequant).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+__all__ = [
+    "PdkError", "lib", "KVPool", "DeviceCSR", "CascadeParams", "CascadePlan", "ChunkedPlan",
+    "partition_indptr", "validate_csr", "parse_switch", "cascade_enabled_from_env",
+    "stacked_head_map", "paged_decode_partial", "merge_states", "decode_flat",
+    "stack_heads", "unstack_heads", "fp8_dequant_bf16",
+    "F32", "BF16", "FP8_E4M3", "DECLINE_NAMES",
+]
+
+F32, BF16, FP8_E4M3 = 0, 1, 2
+DECLINE_NAMES = {0: "none", 1: "disabled", 2: "no_candidate", 3: "members_below_min",
+                 4: "span_below_min", 5: "reaches_last_page"}
+PLAN_FIELDS = {"members": 0, "group_indptr": 1, "span_pages": 2, "l0_indptr": 3,
+               "l0_indices": 4, "l0_len": 5, "l1_indptr": 6, "l1_indices": 7, "l1_len": 8,
+               "merge_indptr": 9, "fused_merge_indptr": 10, "group_of": 11, "member_rank": 12}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpdk.so")
+_lib = None
+
+
+class PdkError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"pdk status {status}: {message}")
+        self.status = status
+
+
+class _Pool(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("num_blocks", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim_k", ctypes.c_int32), ("head_dim_v", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("k_scale", ctypes.c_float),
+                ("v_scale", ctypes.c_float)]
+
+
+class _CSR(ctypes.Structure):
+    _fields_ = [("indptr", ctypes.c_void_p), ("indices", ctypes.c_void_p),
+                ("kv_len", ctypes.c_void_p), ("batch", ctypes.c_int32), ("nnz", ctypes.c_int32)]
+
+
+class _Params(ctypes.Structure):
+    _fields_ = [("enabled", ctypes.c_int32), ("min_shared_pages", ctypes.c_int32),
+                ("min_members", ctypes.c_int32), ("max_groups", ctypes.c_int32),
+                ("l0_partition_tokens", ctypes.c_int32), ("l1_partition_tokens", ctypes.c_int32)]
+
+
+_P, _I, _F, _S, _L = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t, ctypes.c_int64
+_SIGS = {
+    "pdk_partition_indptr": (_I, [_P, _I, _I, _P]),
+    "pdk_validate_csr": (_I, [_P, _I, _I]),
+    "pdk_parse_switch": (_I, [ctypes.c_char_p]),
+    "pdk_cascade_enabled_from_env": (_I, [ctypes.c_char_p]),
+    "pdk_stacked_head_map": (_I, [_I, _I, _I, _P]),
+    "pdk_paged_decode_partial": (_I, [_P, _P, _P, _I, _I, _F, _I, _P, _I, _P, _P, _P]),
+    "pdk_merge_states": (_I, [_P, _P, _I, _P, _I, _I, _I, _P, _P, _P]),
+    "pdk_decode_flat_workspace_bytes": (_S, [_I, _I, _I]),
+    "pdk_decode_flat": (_I, [_P, _P, _P, _I, _I, _F, _I, _P, _I, _P, _P, _P, _S, _P]),
+    "pdk_stack_heads": (_I, [_P, _I, _P, _I, _I, _I, _I, _P, _P]),
+    "pdk_unstack_heads": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P]),
+    "pdk_fp8_dequant_bf16": (_I, [_P, _L, _F, _P, _P]),
+    "pdk_cascade_params_default": (None, [_P]),
+    "pdk_cascade_plan_create": (_I, [_P, _I, _P, _P]),
+    "pdk_cascade_plan_free": (None, [_P]),
+    "pdk_cascade_plan_get": (_I, [_P, _I, _P, _P]),
+    "pdk_cascade_plan_stats": (_I, [_P, _P, _P]),
+    "pdk_cascade_workspace_bytes": (_S, [_P, _I, _I]),
+    "pdk_cascade_plan_upload": (_I, [_P, _P, _S, _P]),
+    "pdk_run_cascade_decode": (_I, [_P, _P, _P, _I, _I, _F, _P, _P, _P, _S, _P]),
+    "pdk_chunked_plan_create": (_I, [_P, _I, _I, _I, _P, _I, _I, _P]),
+    "pdk_chunked_plan_free": (None, [_P]),
+    "pdk_chunked_plan_counts": (_I, [_P, _P]),
+    "pdk_chunked_workspace_bytes": (_S, [_P, _I, _I]),
+    "pdk_chunked_plan_upload": (_I, [_P, _P, _S, _P]),
+    "pdk_run_chunked_decode": (_I, [_P, _P, _P, _P, _I, _I, _F, _P, _P, _P, _P, _P, _S, _P]),
+    "pdk_last_error": (ctypes.c_char_p, []),
+}
+
+
+def lib():
+    """The loaded libpdk.so. Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m paged_split_kv_v2_amd.build`")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = h
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise PdkError(status, lib().pdk_last_error().decode())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    assert t.is_contiguous(), "tensors passed to pdk must be contiguous"
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _np_ptr(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return FP8_E4M3
+    raise TypeError(f"unsupported tensor dtype {t.dtype}")
+
+
+# --------------------------------------------------------------------------
+# Pools and page tables
+# --------------------------------------------------------------------------
+
+@dataclass
+class KVPool:
+    """Device KV pool, HND [num_blocks, Hkv, P, D]; ``v is None`` for a latent
+    pool whose values are the first ``head_dim_v`` lanes of each key row."""
+    k: torch.Tensor
+    v: Optional[torch.Tensor]
+    head_dim_v: int
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+
+    @property
+    def page_size(self) -> int:
+        return int(self.k.shape[2])
+
+    @property
+    def num_kv_heads(self) -> int:
+        return int(self.k.shape[1])
+
+    def struct(self) -> _Pool:
+        return _Pool(self.k.data_ptr(), None if self.v is None else self.v.data_ptr(),
+                     int(self.k.shape[0]), int(self.k.shape[2]), int(self.k.shape[1]),
+                     int(self.k.shape[3]), int(self.head_dim_v), _dtype_code(self.k),
+                     float(self.k_scale), float(self.v_scale))
+
+
+@dataclass
+class DeviceCSR:
+    indptr: torch.Tensor
+    indices: torch.Tensor
+    kv_len: torch.Tensor
+
+    @staticmethod
+    def from_host(indptr, indices, kv_len, device="cuda"):
+        f = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+        idx = np.asarray(indices, dtype=np.int32)
+        if idx.size == 0:
+            idx = np.zeros(1, np.int32)  # keep a valid device pointer
+        return DeviceCSR(f(indptr), f(idx), f(kv_len))
+
+    @property
+    def batch(self) -> int:
+        return int(self.kv_len.shape[0])
+
+    def struct(self) -> _CSR:
+        return _CSR(self.indptr.data_ptr(), self.indices.data_ptr(), self.kv_len.data_ptr(),
+                    self.batch, int(self.indices.numel()))
+
+
+def _host_csr(indptr, indices, kv_len):
+    ip = np.ascontiguousarray(indptr, dtype=np.int32)
+    ix = np.ascontiguousarray(indices, dtype=np.int32)
+    kl = np.ascontiguousarray(kv_len, dtype=np.int32)
+    keep = (ip, ix, kl)
+    s = _CSR(ip.ctypes.data, ix.ctypes.data if ix.size else None, kl.ctypes.data,
+             int(kl.size), int(ip[-1]) if ip.size else 0)
+    return s, keep
+
+
+# --------------------------------------------------------------------------
+# Host-side integer work
+# --------------------------------------------------------------------------
+
+def partition_indptr(kv_len, partition_tokens: int) -> np.ndarray:
+    kl = np.ascontiguousarray(kv_len, dtype=np.int32)
+    out = np.zeros(kl.size + 1, dtype=np.int32)
+    _check(lib().pdk_partition_indptr(_np_ptr(kl), int(kl.size), int(partition_tokens),
+                                      _np_ptr(out)))
+    return out
+
+
+def validate_csr(indptr, indices, kv_len, page_size: int, num_blocks: int):
+    s, keep = _host_csr(indptr, indices, kv_len)
+    _check(lib().pdk_validate_csr(ctypes.byref(s), int(page_size), int(num_blocks)))
+
+
+def parse_switch(value: Optional[str]) -> int:
+    return int(lib().pdk_parse_switch(None if value is None else value.encode()))
+
+
+def cascade_enabled_from_env(var: str) -> int:
+    return int(lib().pdk_cascade_enabled_from_env(var.encode()))
+
+
+def stacked_head_map(members: int, num_kv_heads: int, group: int) -> np.ndarray:
+    out = np.zeros(members * num_kv_heads * group, dtype=np.int32)
+    _check(lib().pdk_stacked_head_map(members, num_kv_heads, group, _np_ptr(out)))
+    return out
+
+
+# --------------------------------------------------------------------------
+# GPU entry points
+# --------------------------------------------------------------------------
+
+def paged_decode_partial(pool: KVPool, csr: DeviceCSR, q: torch.Tensor, sm_scale: float,
+                         partition_tokens: int, part_indptr: torch.Tensor, num_partitions: int,
+                         v_part: Optional[torch.Tensor] = None,
+                         lse_part: Optional[torch.Tensor] = None, stream=None):
+    Hq = int(q.shape[1])
+    if v_part is None:
+        v_part = torch.empty((num_partitions, Hq, pool.head_dim_v), dtype=torch.float32,
+                             device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((num_partitions, Hq), dtype=torch.float32, device=q.device)
+    ps, cs = pool.struct(), csr.struct()
+    _check(lib().pdk_paged_decode_partial(ctypes.byref(ps), ctypes.byref(cs), _ptr(q),
+                                          _dtype_code(q), Hq, float(sm_scale),
+                                          int(partition_tokens), _ptr(part_indptr),
+                                          int(num_partitions), _ptr(v_part), _ptr(lse_part),
+                                          _stream(stream)))
+    return v_part, lse_part
+
+
+def merge_states(v_in: torch.Tensor, lse_in: torch.Tensor, o_indptr: torch.Tensor,
+                 v_out: Optional[torch.Tensor] = None, lse_out: Optional[torch.Tensor] = None,
+                 stream=None, want_lse: bool = True):
+    M = int(o_indptr.shape[0]) - 1
+    H, D = int(v_in.shape[1]), int(v_in.shape[2])
+    if v_out is None:
+        v_out = torch.empty((M, H, D), dtype=torch.float32, device=v_in.device)
+    if lse_out is None and want_lse:
+        lse_out = torch.empty((M, H), dtype=torch.float32, device=v_in.device)
+    _check(lib().pdk_merge_states(_ptr(v_in), _ptr(lse_in), int(v_in.shape[0]), _ptr(o_indptr),
+                                  M, H, D, _ptr(v_out), _ptr(lse_out), _stream(stream)))
+    return v_out, lse_out
+
+
+def decode_flat(pool: KVPool, csr: DeviceCSR, q: torch.Tensor, sm_scale: float,
+                partition_tokens: int, part_indptr: torch.Tensor, num_partitions: int,
+                out: Optional[torch.Tensor] = None, lse_out: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None, stream=None):
+    B, Hq = int(q.shape[0]), int(q.shape[1])
+    need = int(lib().pdk_decode_flat_workspace_bytes(num_partitions, Hq, pool.head_dim_v))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, pool.head_dim_v), dtype=torch.float32, device=q.device)
+    if lse_out is None:
+        lse_out = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    ps, cs = pool.struct(), csr.struct()
+    _check(lib().pdk_decode_flat(ctypes.byref(ps), ctypes.byref(cs), _ptr(q), _dtype_code(q),
+                                 Hq, float(sm_scale), int(partition_tokens), _ptr(part_indptr),
+                                 int(num_partitions), _ptr(out), _ptr(lse_out), _ptr(workspace),
+                                 int(workspace.numel()), _stream(stream)))
+    return out, lse_out
+
+
+def stack_heads(q: torch.Tensor, members: torch.Tensor, num_kv_heads: int, stream=None):
+    M = int(members.numel())
+    Hq, D = int(q.shape[1]), int(q.shape[2])
+    G = Hq // num_kv_heads
+    q0 = torch.empty((M * Hq, D), dtype=q.dtype, device=q.device)
+    _check(lib().pdk_stack_heads(_ptr(q), _dtype_code(q), _ptr(members), M, num_kv_heads, G, D,
+                                 _ptr(q0), _stream(stream)))
+    return q0
+
+
+def unstack_heads(v0: torch.Tensor, lse0: Optional[torch.Tensor], members: int,
+                  num_kv_heads: int, group: int, stream=None):
+    D = int(v0.shape[-1])
+    Hq = num_kv_heads * group
+    v = torch.empty((members, Hq, D), dtype=torch.float32, device=v0.device)
+    l = None if lse0 is None else torch.empty((members, Hq), dtype=torch.float32, device=v0.device)
+    _check(lib().pdk_unstack_heads(_ptr(v0), _ptr(lse0), members, num_kv_heads, group, D,
+                                   _ptr(v), _ptr(l), _stream(stream)))
+    return v, l
+
+
+def fp8_dequant_bf16(codes: torch.Tensor, scale: float, stream=None) -> torch.Tensor:
+    out = torch.empty(codes.shape, dtype=torch.int16, device=codes.device)
+    _check(lib().pdk_fp8_dequant_bf16(_ptr(codes), int(codes.numel()), float(scale), _ptr(out),
+                                      _stream(stream)))
+    return out
+
+
+# --------------------------------------------------------------------------
+# Cascade decode
+# --------------------------------------------------------------------------
+
+@dataclass
+class CascadeParams:
+    enabled: int = -1
+    min_shared_pages: int = 16
+    min_members: int = 2
+    max_groups: int = 1
+    l0_partition_tokens: int = 256
+    l1_partition_tokens: int = 512
+
+    def struct(self) -> _Params:
+        return _Params(self.enabled, self.min_shared_pages, self.min_members, self.max_groups,
+                       self.l0_partition_tokens, self.l1_partition_tokens)
+
+
+class CascadePlan:
+    """A cascade plan built by the library's C++ planner from a HOST page table."""
+
+    def __init__(self, indptr, indices, kv_len, page_size: int, params: CascadeParams):
+        s, keep = _host_csr(indptr, indices, kv_len)
+        p = params.struct()
+        h = ctypes.c_void_p()
+        _check(lib().pdk_cascade_plan_create(ctypes.byref(s), int(page_size), ctypes.byref(p),
+                                             ctypes.byref(h)))
+        self._h = h
+        self.params = params
+        self.workspace = None
+
+    def __del__(self):
+        if getattr(self, "_h", None) and _lib is not None:
+            _lib.pdk_cascade_plan_free(self._h)
+            self._h = None
+
+    def field(self, name: str) -> np.ndarray:
+        data = ctypes.POINTER(ctypes.c_int32)()
+        n = ctypes.c_int32()
+        _check(lib().pdk_cascade_plan_get(self._h, PLAN_FIELDS[name], ctypes.byref(data),
+                                          ctypes.byref(n)))
+        return np.ctypeslib.as_array(data, shape=(n.value,)).copy() if n.value else \
+            np.zeros(0, np.int32)
+
+    def stats(self):
+        st = (ctypes.c_int32 * 6)()
+        dec = ctypes.c_int32()
+        _check(lib().pdk_cascade_plan_stats(self._h, st, ctypes.byref(dec)))
+        keys = ("batch", "members", "shared_pages", "shared_tokens", "prefix_chunks",
+                "suffix_chunks")
+        return dict(zip(keys, list(st))), DECLINE_NAMES[dec.value]
+
+    def workspace_bytes(self, num_q_heads: int, head_dim_v: int) -> int:
+        return int(lib().pdk_cascade_workspace_bytes(self._h, num_q_heads, head_dim_v))
+
+    def upload(self, num_q_heads: int, head_dim_v: int, device="cuda", stream=None,
+               workspace: Optional[torch.Tensor] = None):
+        need = self.workspace_bytes(num_q_heads, head_dim_v)
+        if workspace is None:
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+        _check(lib().pdk_cascade_plan_upload(self._h, _ptr(workspace), int(workspace.numel()),
+                                             _stream(stream)))
+        self.workspace = workspace
+        return workspace
+
+    def run(self, pool: KVPool, q: torch.Tensor, sm_scale: float,
+            out: Optional[torch.Tensor] = None, lse_out: Optional[torch.Tensor] = None,
+            stream=None):
+        B, Hq = int(q.shape[0]), int(q.shape[1])
+        if self.workspace is None:
+            self.upload(Hq, pool.head_dim_v, q.device, stream)
+        if out is None:
+            out = torch.empty((B, Hq, pool.head_dim_v), dtype=torch.float32, device=q.device)
+        if lse_out is None:
+            lse_out = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+        ps = pool.struct()
+        _check(lib().pdk_run_cascade_decode(self._h, ctypes.byref(ps), _ptr(q), _dtype_code(q),
+                                            Hq, float(sm_scale), _ptr(out), _ptr(lse_out),
+                                            _ptr(self.workspace), int(self.workspace.numel()),
+                                            _stream(stream)))
+        return out, lse_out
+
+
+# --------------------------------------------------------------------------
+# Chunked cached prefix + new suffix
+# --------------------------------------------------------------------------
+
+class ChunkedPlan:
+    def __init__(self, prefix_csr, prefix_page_size: int, chunk_tokens: int,
+                 prefix_partition_tokens: int, suffix_csr, suffix_page_size: int,
+                 suffix_partition_tokens: int):
+        s1, k1 = _host_csr(*prefix_csr)
+        s2, k2 = _host_csr(*suffix_csr)
+        h = ctypes.c_void_p()
+        _check(lib().pdk_chunked_plan_create(ctypes.byref(s1), int(prefix_page_size),
+                                             int(chunk_tokens), int(prefix_partition_tokens),
+                                             ctypes.byref(s2), int(suffix_page_size),
+                                             int(suffix_partition_tokens), ctypes.byref(h)))
+        self._h = h
+        self.workspace = None
+
+    def __del__(self):
+        if getattr(self, "_h", None) and _lib is not None:
+            _lib.pdk_chunked_plan_free(self._h)
+            self._h = None
+
+    def counts(self):
+        c = (ctypes.c_int32 * 4)()
+        _check(lib().pdk_chunked_plan_counts(self._h, c))
+        return dict(zip(("batch", "chunks", "prefix_partitions", "suffix_partitions"), list(c)))
+
+    def upload(self, num_q_heads: int, head_dim_v: int, device="cuda", stream=None):
+        need = int(lib().pdk_chunked_workspace_bytes(self._h, num_q_heads, head_dim_v))
+        self.workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+        _check(lib().pdk_chunked_plan_upload(self._h, _ptr(self.workspace),
+                                             int(self.workspace.numel()), _stream(stream)))
+        return self.workspace
+
+    def run(self, prefix_pool: KVPool, suffix_pool: KVPool, q: torch.Tensor, sm_scale: float,
+            out=None, lse_out=None, chunk_out=None, chunk_lse=None, stream=None):
+        B, Hq = int(q.shape[0]), int(q.shape[1])
+        Dv = prefix_pool.head_dim_v
+        if self.workspace is None:
+            self.upload(Hq, Dv, q.device, stream)
+        if out is None:
+            out = torch.empty((B, Hq, Dv), dtype=torch.float32, device=q.device)
+        if lse_out is None:
+            lse_out = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+        p1, p2 = prefix_pool.struct(), suffix_pool.struct()
+        _check(lib().pdk_run_chunked_decode(self._h, ctypes.byref(p1), ctypes.byref(p2), _ptr(q),
+                                            _dtype_code(q), Hq, float(sm_scale), _ptr(out),
+                                            _ptr(lse_out), _ptr(chunk_out), _ptr(chunk_lse),
+                                            _ptr(self.workspace), int(self.workspace.numel()),
+                                            _stream(stream)))
+        return out, lse_out

@@ -1,0 +1,82 @@
+// Internal declarations shared by the host library and the HIP kernels.
+// Not part of the public ABI (see include/pdk.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pdk.h"
+
+namespace pdk {
+
+// Arguments of one partial-state launch over a page-table "view".
+//
+// A view is a CSR page table plus partitions over it. In a flat (or
+// level-1) launch, request b of the view is batch request b and owns
+// G = Hq/Hkv query rows per KV head. In a stacked (level-0) launch, view
+// request k is a group of members; it owns M_k * G query rows per KV head,
+// row j = m*G + g taking member m's query head kv*G + g (KV-head-major
+// stacking), and each member's partials go to that member's own output rows.
+struct PartialArgs {
+  // pool
+  const void* k;
+  const void* v;              // nullptr: latent pool, V = first Dv lanes of K
+  long long k_bstride;        // elements between pool rows (blocks)
+  long long k_hstride;        // elements between KV heads of a row
+  long long v_bstride, v_hstride;
+  int num_blocks, P, Hkv, Dk, Dv;
+  int p_shift;                // log2(P) when P is a power of two, else -1
+  int kv_dtype;
+  float k_scale, v_scale;
+  // view
+  const int* indptr;
+  const int* indices;
+  const int* kv_len;
+  int batch;
+  const int* part_indptr;     // [batch+1] partitions of the view
+  int num_parts;
+  int S;                      // partition tokens
+  // queries
+  const void* q;              // [*, Hq, Dk]
+  int q_dtype;
+  int Hq;
+  int G;                      // query heads per KV head of the batch layout
+  float scale_log2;           // sm_scale * log2(e)
+  // stacking; member_indptr == nullptr for a flat view
+  const int* member_indptr;   // [batch+1] members of view request k
+  const int* members;         // batch index of each member slot
+  int max_rows;               // max query rows per KV head over the view
+  // outputs [rows, Hq, Dv] and [rows, Hq]
+  const int* out_row_base;    // flat: indexed by b; stacked: by member slot
+  float* v_out;
+  float* lse_out;
+};
+
+int launch_partial(const PartialArgs& a, hipStream_t stream);
+int launch_partial_valu(const PartialArgs& a, hipStream_t stream);
+int valu_max_rows(int head_dim);
+// out_stride: output row i is written at row i * out_stride of v_out / lse_out
+int launch_merge(const float* v_in, const float* lse_in, int num_in, const int* o_indptr,
+                 int num_out, int H, int D, float* v_out, float* lse_out, int out_stride,
+                 hipStream_t stream);
+
+// Checked entry points used by the plan runners (same checks as the public
+// pdk_paged_decode_partial / pdk_merge_states, plus stacking and row maps).
+int partial_rows(const pdk_kv_pool* pool, const pdk_csr* view, const void* q, int q_dtype, int Hq,
+                 float sm_scale, int S, const int* part_indptr, int num_parts,
+                 const int* member_indptr, const int* members, int max_members, int G,
+                 const int* out_row_base, float* v_out, float* lse_out, hipStream_t stream);
+int merge_rows(const float* v_in, const float* lse_in, int num_in, const int* o_indptr,
+               int num_out, int H, int D, float* v_out, float* lse_out, int out_stride,
+               hipStream_t stream);
+int launch_stack(const void* q, int q_dtype, const int* members, int M, int Hkv, int G, int D,
+                 void* q0, hipStream_t stream);
+int launch_unstack(const float* v0, const float* lse0, int M, int Hkv, int G, int D,
+                   float* v_out, float* lse_out, hipStream_t stream);
+int launch_dequant(const uint8_t* in, long long n, float scale, uint16_t* out,
+                   hipStream_t stream);
+
+// error reporting (thread-local message, see pdk_last_error)
+int fail(int status, const char* fmt, ...);
+
+}  // namespace pdk

@@ -1,0 +1,546 @@
+// Cascade (shared-prefix) planning and launch, and the chunked-prefix plan.
+//
+// Cascade [cascade-PR = mlxcel pull request "perf(core): compute shared
+// prompt prefixes once per decode batch"]:
+//   * "Detection reads the page table, not the refcounts": equal pool rows at
+//     equal positions of two page lists are the same bytes, so sharing is
+//     found by comparing the host CSR positionally.
+//   * "Task items" 1: candidates grouped by first page; each group's span is
+//     the longest common page prefix (a member that diverges early shortens
+//     the span); the subgroup that removes the most page reads,
+//     span * (members - 1), is chosen; one shared level.
+//   * "Task items" 2: level 0 is a one-request view over the span; level 1 is
+//     the whole batch with the members' span pages removed; non-members keep
+//     their whole range and a merge group of one.
+//   * "Task items" 4 and "Correctness coverage": shared pages must be full; a
+//     span that reaches a member's last page, or is below the page or member
+//     threshold, falls back to the flat launch.
+//   * "Proving which path a benchmark arm took": the outcome carries batch,
+//     members, shared pages/tokens, prefix/suffix chunk counts, or a reason.
+// Readings where the page is silent: members ordered by batch index; a span
+// equal to a member's page count rejects the group; checks in the order
+// member count, span, last page; ties in score go to the lowest first batch
+// index; max_groups 0/k extends the single-subgroup rule; the reported
+// decline reason is that of the best-scoring rejected group.
+//
+// Launch layout: every request's partial rows are contiguous,
+// [level-0 partitions (members only)][level-1 partitions], so that one
+// merge per request equals the page's level merge followed by the pair merge
+// (the merge is associative: "How the #898 merge kernel is reused").
+//
+// Chunked prefix [DCP-PR = ROCm/ATOM pull request "[feat][DCP] Optimize MLA
+// DCP ...", section 3.2 figure]: the cached range is cut into chunks, each
+// chunk yields (O, LSE), the chunk states are merged, and the result is
+// merged with the new-token (suffix) state.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <map>
+#include <vector>
+
+#include "internal.h"
+#include "pdk.h"
+
+using namespace pdk;
+
+namespace {
+
+int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// A set of int32 host arrays uploaded as one blob to the head of a workspace.
+struct Blob {
+  std::vector<int32_t> data;
+  size_t add(const std::vector<int32_t>& v) {
+    const size_t off = data.size();
+    data.insert(data.end(), v.begin(), v.end());
+    while (data.size() % 64) data.push_back(0);  // keep every array 256-byte aligned
+    return off;
+  }
+  size_t bytes() const { return data.size() * sizeof(int32_t); }
+};
+
+struct Candidate {
+  std::vector<int32_t> members;
+  int32_t span;
+  long long score;
+  int32_t reason;
+};
+
+}  // namespace
+
+struct pdk_cascade_plan {
+  int32_t batch = 0, page_size = 0;
+  pdk_cascade_params params{};
+  int32_t decline = PDK_DECLINE_NONE;
+  int32_t stats[6] = {0, 0, 0, 0, 0, 0};
+  std::vector<int32_t> f[PDK_PLAN_NUM_FIELDS];
+  // launch bookkeeping
+  std::vector<int32_t> l0_part_indptr, l1_part_indptr, member_row_base, l1_row_base;
+  int32_t n_groups = 0, n_l0_parts = 0, n_l1_parts = 0, total_rows = 0, max_members = 0;
+  Blob blob;
+  struct {
+    size_t l0_indptr, l0_indices, l0_len, l0_parts, group_indptr, members, member_rows;
+    size_t l1_indptr, l1_indices, l1_len, l1_parts, l1_rows, fused;
+  } off{};
+  const void* uploaded_to = nullptr;
+};
+
+extern "C" {
+
+void pdk_cascade_params_default(pdk_cascade_params* p) {
+  if (!p) return;
+  p->enabled = -1;
+  p->min_shared_pages = 16;
+  p->min_members = 2;
+  p->max_groups = 1;
+  p->l0_partition_tokens = 256;
+  p->l1_partition_tokens = 512;
+}
+
+int pdk_cascade_plan_create(const pdk_csr* csr, int32_t P, const pdk_cascade_params* params,
+                            pdk_cascade_plan** plan_out) {
+  if (!plan_out || !params) return fail(PDK_ERR_ARG, "NULL plan_out/params");
+  *plan_out = nullptr;
+  int st = pdk_validate_csr(csr, P, 0x7FFFFFFF);
+  if (st) return st;
+  const pdk_cascade_params& pr = *params;
+  if (pr.min_shared_pages < 1 || pr.min_members < 2 || pr.max_groups < 0)
+    return fail(PDK_ERR_ARG, "thresholds: min_shared_pages >= 1, min_members >= 2, max_groups >= 0");
+  if (pr.l0_partition_tokens <= 0 || pr.l0_partition_tokens % P ||
+      pr.l1_partition_tokens <= 0 || pr.l1_partition_tokens % P)
+    return fail(PDK_ERR_ARG, "partition sizes must be positive multiples of page_size %d", P);
+
+  const int B = csr->batch;
+  const int32_t* indptr = csr->indptr;
+  const int32_t* idx = csr->indices;
+  const int32_t* len = csr->kv_len;
+  auto plan = new pdk_cascade_plan();
+  plan->batch = B;
+  plan->page_size = P;
+  plan->params = pr;
+
+  std::vector<Candidate> chosen;
+  if (pr.enabled != 1) {
+    plan->decline = PDK_DECLINE_DISABLED;
+  } else {
+    // group candidates by first page, members in batch order
+    std::map<int32_t, std::vector<int32_t>> by_first;
+    std::vector<int32_t> order;  // first ids in order of first appearance
+    for (int b = 0; b < B; ++b) {
+      if (indptr[b + 1] - indptr[b] < 1 || len[b] < 1) continue;
+      auto it = by_first.find(idx[indptr[b]]);
+      if (it == by_first.end()) order.push_back(idx[indptr[b]]);
+      by_first[idx[indptr[b]]].push_back(b);
+    }
+    std::vector<Candidate> cands;
+    for (int32_t first : order) {
+      const auto& mem = by_first[first];
+      if (mem.size() < 2) continue;
+      // longest common page prefix, position by position
+      int32_t lcp = 0;
+      for (;;) {
+        bool ok = true;
+        for (int32_t b : mem)
+          if (lcp >= indptr[b + 1] - indptr[b] || idx[indptr[b] + lcp] != idx[indptr[mem[0]] + lcp]) {
+            ok = false;
+            break;
+          }
+        if (!ok) break;
+        ++lcp;
+      }
+      // every shared page full
+      int32_t span = lcp;
+      for (int32_t b : mem) span = std::min(span, len[b] / P);
+      Candidate c{mem, span, (long long)span * (long long)(mem.size() - 1), PDK_DECLINE_NONE};
+      if ((int)mem.size() < pr.min_members) c.reason = PDK_DECLINE_MEMBERS_BELOW_MIN;
+      else if (span < pr.min_shared_pages) c.reason = PDK_DECLINE_SPAN_BELOW_MIN;
+      else
+        for (int32_t b : mem)
+          if (span == indptr[b + 1] - indptr[b]) { c.reason = PDK_DECLINE_REACHES_LAST_PAGE; break; }
+      cands.push_back(std::move(c));
+    }
+    auto better = [](const Candidate& x, const Candidate& y) {
+      if (x.score != y.score) return x.score > y.score;
+      return x.members[0] < y.members[0];
+    };
+    std::vector<Candidate> ok;
+    for (auto& c : cands)
+      if (c.reason == PDK_DECLINE_NONE) ok.push_back(c);
+    if (cands.empty()) {
+      plan->decline = PDK_DECLINE_NO_CANDIDATE;
+    } else if (ok.empty()) {
+      std::sort(cands.begin(), cands.end(), better);
+      plan->decline = cands[0].reason;
+    } else {
+      std::sort(ok.begin(), ok.end(), better);
+      const size_t take = pr.max_groups == 0 ? ok.size() : std::min(ok.size(), (size_t)pr.max_groups);
+      chosen.assign(ok.begin(), ok.begin() + take);
+      std::sort(chosen.begin(), chosen.end(),
+                [](const Candidate& x, const Candidate& y) { return x.members[0] < y.members[0]; });
+    }
+  }
+
+  auto& F = plan->f;
+  const int K = (int)chosen.size();
+  plan->n_groups = K;
+  std::vector<int32_t> group_of(B, -1), rank(B, -1), span_of(B, 0);
+  F[PDK_PLAN_GROUP_INDPTR].push_back(0);
+  F[PDK_PLAN_L0_INDPTR].push_back(0);
+  for (int k = 0; k < K; ++k) {
+    const auto& c = chosen[k];
+    for (size_t m = 0; m < c.members.size(); ++m) {
+      group_of[c.members[m]] = k;
+      rank[c.members[m]] = (int32_t)m;
+      span_of[c.members[m]] = c.span;
+      F[PDK_PLAN_MEMBERS].push_back(c.members[m]);
+    }
+    F[PDK_PLAN_GROUP_INDPTR].push_back((int32_t)F[PDK_PLAN_MEMBERS].size());
+    F[PDK_PLAN_SPAN_PAGES].push_back(c.span);
+    const int b0 = c.members[0];
+    for (int i = 0; i < c.span; ++i) F[PDK_PLAN_L0_INDICES].push_back(idx[indptr[b0] + i]);
+    F[PDK_PLAN_L0_INDPTR].push_back((int32_t)F[PDK_PLAN_L0_INDICES].size());
+    F[PDK_PLAN_L0_LEN].push_back(c.span * P);
+    plan->max_members = std::max(plan->max_members, (int32_t)c.members.size());
+  }
+  F[PDK_PLAN_L1_INDPTR].push_back(0);
+  F[PDK_PLAN_MERGE_INDPTR].push_back(0);
+  for (int b = 0; b < B; ++b) {
+    const int s = span_of[b];
+    for (int i = indptr[b] + s; i < indptr[b + 1]; ++i) F[PDK_PLAN_L1_INDICES].push_back(idx[i]);
+    F[PDK_PLAN_L1_INDPTR].push_back((int32_t)F[PDK_PLAN_L1_INDICES].size());
+    F[PDK_PLAN_L1_LEN].push_back(len[b] - s * P);
+    F[PDK_PLAN_MERGE_INDPTR].push_back(F[PDK_PLAN_MERGE_INDPTR].back() + (group_of[b] >= 0 ? 2 : 1));
+  }
+  F[PDK_PLAN_GROUP_OF] = group_of;
+  F[PDK_PLAN_MEMBER_RANK] = rank;
+
+  // partitions of both levels and the fused row layout
+  const int S0 = pr.l0_partition_tokens, S1 = pr.l1_partition_tokens;
+  plan->l0_part_indptr.assign(1, 0);
+  for (int k = 0; k < K; ++k)
+    plan->l0_part_indptr.push_back(plan->l0_part_indptr.back() + ceil_div(F[PDK_PLAN_L0_LEN][k], S0));
+  plan->l1_part_indptr.assign(1, 0);
+  for (int b = 0; b < B; ++b)
+    plan->l1_part_indptr.push_back(plan->l1_part_indptr.back() + ceil_div(F[PDK_PLAN_L1_LEN][b], S1));
+  plan->n_l0_parts = plan->l0_part_indptr.back();
+  plan->n_l1_parts = plan->l1_part_indptr.back();
+  auto& fused = F[PDK_PLAN_FUSED_MERGE_INDPTR];
+  fused.assign(1, 0);
+  plan->l1_row_base.resize(B);
+  std::vector<int32_t> row_start(B);
+  for (int b = 0; b < B; ++b) {
+    const int k = group_of[b];
+    const int n0 = k >= 0 ? plan->l0_part_indptr[k + 1] - plan->l0_part_indptr[k] : 0;
+    const int n1 = plan->l1_part_indptr[b + 1] - plan->l1_part_indptr[b];
+    row_start[b] = fused.back();
+    plan->l1_row_base[b] = fused.back() + n0;
+    fused.push_back(fused.back() + n0 + n1);
+  }
+  plan->total_rows = fused.back();
+  plan->member_row_base.clear();
+  for (int32_t b : F[PDK_PLAN_MEMBERS]) plan->member_row_base.push_back(row_start[b]);
+
+  long long shared = 0, pre_chunks = 0, suf_chunks = 0;
+  for (int k = 0; k < K; ++k) {
+    shared += F[PDK_PLAN_SPAN_PAGES][k];
+    pre_chunks += ceil_div((long long)F[PDK_PLAN_SPAN_PAGES][k] * P, S0);
+  }
+  for (int b = 0; b < B; ++b) suf_chunks += ceil_div(F[PDK_PLAN_L1_LEN][b], S1);
+  plan->stats[0] = B;
+  plan->stats[1] = (int32_t)F[PDK_PLAN_MEMBERS].size();
+  plan->stats[2] = (int32_t)shared;
+  plan->stats[3] = (int32_t)(shared * P);
+  plan->stats[4] = (int32_t)pre_chunks;
+  plan->stats[5] = (int32_t)suf_chunks;
+
+  // device blob (uploaded to the head of the workspace)
+  auto& bl = plan->blob;
+  plan->off.l0_indptr = bl.add(F[PDK_PLAN_L0_INDPTR]);
+  plan->off.l0_indices = bl.add(F[PDK_PLAN_L0_INDICES]);
+  plan->off.l0_len = bl.add(F[PDK_PLAN_L0_LEN]);
+  plan->off.l0_parts = bl.add(plan->l0_part_indptr);
+  plan->off.group_indptr = bl.add(F[PDK_PLAN_GROUP_INDPTR]);
+  plan->off.members = bl.add(F[PDK_PLAN_MEMBERS]);
+  plan->off.member_rows = bl.add(plan->member_row_base);
+  plan->off.l1_indptr = bl.add(F[PDK_PLAN_L1_INDPTR]);
+  plan->off.l1_indices = bl.add(F[PDK_PLAN_L1_INDICES]);
+  plan->off.l1_len = bl.add(F[PDK_PLAN_L1_LEN]);
+  plan->off.l1_parts = bl.add(plan->l1_part_indptr);
+  plan->off.l1_rows = bl.add(plan->l1_row_base);
+  plan->off.fused = bl.add(fused);
+  *plan_out = plan;
+  return PDK_OK;
+}
+
+void pdk_cascade_plan_free(pdk_cascade_plan* plan) { delete plan; }
+
+int pdk_cascade_plan_get(const pdk_cascade_plan* plan, int32_t field, const int32_t** data,
+                         int32_t* len) {
+  if (!plan || !data || !len) return fail(PDK_ERR_ARG, "NULL argument");
+  if (field < 0 || field >= PDK_PLAN_NUM_FIELDS) return fail(PDK_ERR_ARG, "unknown field %d", field);
+  *data = plan->f[field].data();
+  *len = (int32_t)plan->f[field].size();
+  return PDK_OK;
+}
+
+int pdk_cascade_plan_stats(const pdk_cascade_plan* plan, int32_t stats[6], int32_t* decline) {
+  if (!plan) return fail(PDK_ERR_ARG, "NULL plan");
+  if (stats)
+    for (int i = 0; i < 6; ++i) stats[i] = plan->stats[i];
+  if (decline) *decline = plan->decline;
+  return PDK_OK;
+}
+
+static size_t cascade_state_offset(const pdk_cascade_plan* plan) { return align256(plan->blob.bytes()); }
+
+size_t pdk_cascade_workspace_bytes(const pdk_cascade_plan* plan, int32_t Hq, int32_t Dv) {
+  if (!plan || Hq <= 0 || Dv <= 0) return 0;
+  const size_t rows = (size_t)plan->total_rows * Hq;
+  return cascade_state_offset(plan) + align256(rows * Dv * sizeof(float)) + rows * sizeof(float);
+}
+
+int pdk_cascade_plan_upload(pdk_cascade_plan* plan, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!plan || !ws) return fail(PDK_ERR_ARG, "NULL plan/workspace");
+  if (ws_bytes < plan->blob.bytes())
+    return fail(PDK_ERR_WORKSPACE, "workspace %zu bytes < plan %zu", ws_bytes, plan->blob.bytes());
+  if (plan->blob.bytes() > 0) {
+    hipError_t e = hipMemcpyAsync(ws, plan->blob.data.data(), plan->blob.bytes(),
+                                  hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return fail(PDK_ERR_HIP, "plan upload: %s", hipGetErrorString(e));
+  }
+  plan->uploaded_to = ws;
+  return PDK_OK;
+}
+
+int pdk_run_cascade_decode(const pdk_cascade_plan* plan, const pdk_kv_pool* pool, const void* q,
+                           int32_t q_dtype, int32_t Hq, float sm_scale, float* out,
+                           float* lse_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!plan || !pool || !q || !out || !ws) return fail(PDK_ERR_ARG, "NULL argument");
+  if (pool->page_size != plan->page_size)
+    return fail(PDK_ERR_SHAPE, "pool page size %d != plan page size %d", pool->page_size,
+                plan->page_size);
+  if (plan->uploaded_to != ws)
+    return fail(PDK_ERR_WORKSPACE, "plan was not uploaded to this workspace");
+  const size_t need = pdk_cascade_workspace_bytes(plan, Hq, pool->head_dim_v);
+  if (ws_bytes < need) return fail(PDK_ERR_WORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
+  if (Hq <= 0 || Hq % pool->num_kv_heads) return fail(PDK_ERR_SHAPE, "num_q_heads %d", Hq);
+  const int32_t* base = (const int32_t*)ws;
+  const auto& o = plan->off;
+  float* v_part = (float*)((char*)ws + cascade_state_offset(plan));
+  float* lse_part = (float*)((char*)v_part + align256((size_t)plan->total_rows * Hq * pool->head_dim_v * 4));
+  const int G = Hq / pool->num_kv_heads;
+
+  // level 1: every request's remaining range (the flat batch when declined)
+  if (plan->n_l1_parts > 0) {
+    pdk_csr v1{base + o.l1_indptr, base + o.l1_indices, base + o.l1_len, plan->batch, 0};
+    int st = partial_rows(pool, &v1, q, q_dtype, Hq, sm_scale,
+                                           plan->params.l1_partition_tokens, base + o.l1_parts,
+                                           plan->n_l1_parts, nullptr, nullptr, 0, G,
+                                           base + o.l1_rows, v_part, lse_part, stream);
+    if (st) return st;
+  }
+  // level 0: each selected group's span once, members stacked KV-head-major
+  if (plan->n_l0_parts > 0) {
+    pdk_csr v0{base + o.l0_indptr, base + o.l0_indices, base + o.l0_len, plan->n_groups, 0};
+    int st = partial_rows(pool, &v0, q, q_dtype, Hq, sm_scale,
+                                           plan->params.l0_partition_tokens, base + o.l0_parts,
+                                           plan->n_l0_parts, base + o.group_indptr,
+                                           base + o.members, plan->max_members, G,
+                                           base + o.member_rows, v_part, lse_part, stream);
+    if (st) return st;
+  }
+  return pdk_merge_states(v_part, lse_part, plan->total_rows, base + o.fused, plan->batch, Hq,
+                          pool->head_dim_v, out, lse_out, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Chunked cached prefix + new suffix [DCP-PR, section 3.2 figure]
+// ---------------------------------------------------------------------------
+
+}  // extern "C"
+
+struct pdk_chunked_plan {
+  int32_t batch = 0, n_chunks = 0, n_pre_parts = 0, n_suf_parts = 0;
+  int32_t P = 0, C = 0, S = 0, Ps = 0, Ss = 0;
+  Blob blob;
+  struct {
+    size_t ch_indptr, ch_indices, ch_len, ch_parts, ch_slots, ch_owner, req_chunks;
+    size_t suf_indptr, suf_indices, suf_len, suf_parts, pair;
+  } off{};
+  const void* uploaded_to = nullptr;
+};
+
+namespace {
+
+// byte offsets of the float regions behind the integer blob
+struct ChunkedLayout {
+  size_t v_pre, l_pre, v_suf, l_suf, v_ch, l_ch, v_pair, l_pair, total;
+};
+
+ChunkedLayout chunked_layout(const pdk_chunked_plan* p, int Hq, int Dv) {
+  ChunkedLayout L{};
+  size_t o = align256(p->blob.bytes());
+  auto take = [&](size_t rows, size_t width) {
+    const size_t at = o;
+    o += align256(rows * width * sizeof(float));
+    return at;
+  };
+  L.v_pre = take((size_t)p->n_pre_parts * Hq, Dv);
+  L.l_pre = take((size_t)p->n_pre_parts * Hq, 1);
+  L.v_suf = take((size_t)p->n_suf_parts * Hq, Dv);
+  L.l_suf = take((size_t)p->n_suf_parts * Hq, 1);
+  L.v_ch = take((size_t)p->n_chunks * Hq, Dv);
+  L.l_ch = take((size_t)p->n_chunks * Hq, 1);
+  L.v_pair = take((size_t)2 * p->batch * Hq, Dv);
+  L.l_pair = take((size_t)2 * p->batch * Hq, 1);
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pdk_chunked_plan_create(const pdk_csr* pre, int32_t P, int32_t C, int32_t S,
+                            const pdk_csr* suf, int32_t Ps, int32_t Ss,
+                            pdk_chunked_plan** plan_out) {
+  if (!plan_out) return fail(PDK_ERR_ARG, "NULL plan_out");
+  *plan_out = nullptr;
+  int st = pdk_validate_csr(pre, P, 0x7FFFFFFF);
+  if (st) return st;
+  if ((st = pdk_validate_csr(suf, Ps, 0x7FFFFFFF))) return st;
+  if (pre->batch != suf->batch)
+    return fail(PDK_ERR_SHAPE, "prefix batch %d != suffix batch %d", pre->batch, suf->batch);
+  if (C <= 0 || C % P || S <= 0 || S % P || Ss <= 0 || Ss % Ps)
+    return fail(PDK_ERR_ARG, "chunk/partition sizes must be positive multiples of the page sizes");
+  auto plan = new pdk_chunked_plan();
+  const int B = pre->batch;
+  plan->batch = B;
+  plan->P = P; plan->C = C; plan->S = S; plan->Ps = Ps; plan->Ss = Ss;
+  std::vector<int32_t> ch_indptr{0}, ch_indices, ch_len, ch_parts{0}, ch_slots{0}, owner,
+      req_chunks{0}, suf_parts{0}, pair;
+  for (int b = 0; b < B; ++b) {
+    const int n = pre->kv_len[b];
+    const int nch = ceil_div(n, C);
+    for (int c = 0; c < nch; ++c) {
+      const int a = c * C, e = std::min(n, (c + 1) * C);
+      for (int pg = a / P; pg < ceil_div(e, P); ++pg) ch_indices.push_back(pre->indices[pre->indptr[b] + pg]);
+      ch_indptr.push_back((int32_t)ch_indices.size());
+      ch_len.push_back(e - a);
+      ch_parts.push_back(ch_parts.back() + ceil_div(e - a, S));
+      ch_slots.push_back((int32_t)owner.size() + 1);
+      owner.push_back(b);
+    }
+    req_chunks.push_back(req_chunks.back() + nch);
+    suf_parts.push_back(suf_parts.back() + ceil_div(suf->kv_len[b], Ss));
+  }
+  for (int b = 0; b <= B; ++b) pair.push_back(2 * b);
+  plan->n_chunks = (int32_t)owner.size();
+  plan->n_pre_parts = ch_parts.back();
+  plan->n_suf_parts = suf_parts.back();
+  auto& bl = plan->blob;
+  plan->off.ch_indptr = bl.add(ch_indptr);
+  plan->off.ch_indices = bl.add(ch_indices);
+  plan->off.ch_len = bl.add(ch_len);
+  plan->off.ch_parts = bl.add(ch_parts);
+  plan->off.ch_slots = bl.add(ch_slots);
+  plan->off.ch_owner = bl.add(owner);
+  plan->off.req_chunks = bl.add(req_chunks);
+  plan->off.suf_indptr = bl.add(std::vector<int32_t>(suf->indptr, suf->indptr + B + 1));
+  plan->off.suf_indices = bl.add(std::vector<int32_t>(suf->indices, suf->indices + suf->nnz));
+  plan->off.suf_len = bl.add(std::vector<int32_t>(suf->kv_len, suf->kv_len + B));
+  plan->off.suf_parts = bl.add(suf_parts);
+  plan->off.pair = bl.add(pair);
+  *plan_out = plan;
+  return PDK_OK;
+}
+
+void pdk_chunked_plan_free(pdk_chunked_plan* plan) { delete plan; }
+
+int pdk_chunked_plan_counts(const pdk_chunked_plan* plan, int32_t counts[4]) {
+  if (!plan || !counts) return fail(PDK_ERR_ARG, "NULL argument");
+  counts[0] = plan->batch;
+  counts[1] = plan->n_chunks;
+  counts[2] = plan->n_pre_parts;
+  counts[3] = plan->n_suf_parts;
+  return PDK_OK;
+}
+
+size_t pdk_chunked_workspace_bytes(const pdk_chunked_plan* plan, int32_t Hq, int32_t Dv) {
+  if (!plan || Hq <= 0 || Dv <= 0) return 0;
+  return chunked_layout(plan, Hq, Dv).total;
+}
+
+int pdk_chunked_plan_upload(pdk_chunked_plan* plan, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!plan || !ws) return fail(PDK_ERR_ARG, "NULL plan/workspace");
+  if (ws_bytes < plan->blob.bytes())
+    return fail(PDK_ERR_WORKSPACE, "workspace %zu bytes < plan %zu", ws_bytes, plan->blob.bytes());
+  hipError_t e = hipMemcpyAsync(ws, plan->blob.data.data(), plan->blob.bytes(),
+                                hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return fail(PDK_ERR_HIP, "plan upload: %s", hipGetErrorString(e));
+  plan->uploaded_to = ws;
+  return PDK_OK;
+}
+
+int pdk_run_chunked_decode(const pdk_chunked_plan* plan, const pdk_kv_pool* pre_pool,
+                           const pdk_kv_pool* suf_pool, const void* q, int32_t q_dtype,
+                           int32_t Hq, float sm_scale, float* out, float* lse_out,
+                           float* chunk_out, float* chunk_lse, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  if (!plan || !pre_pool || !suf_pool || !q || !out || !ws) return fail(PDK_ERR_ARG, "NULL argument");
+  if (plan->uploaded_to != ws)
+    return fail(PDK_ERR_WORKSPACE, "plan was not uploaded to this workspace");
+  if (pre_pool->page_size != plan->P || suf_pool->page_size != plan->Ps)
+    return fail(PDK_ERR_SHAPE, "pool page sizes do not match the plan");
+  const int Dv = pre_pool->head_dim_v;
+  if (suf_pool->head_dim_v != Dv || suf_pool->head_dim_k != pre_pool->head_dim_k ||
+      suf_pool->num_kv_heads != pre_pool->num_kv_heads)
+    return fail(PDK_ERR_SHAPE, "prefix and suffix pools disagree on heads or head dims");
+  if ((!chunk_out) != (!chunk_lse)) return fail(PDK_ERR_ARG, "chunk_out/chunk_lse: both or neither");
+  if (Hq <= 0 || Hq % pre_pool->num_kv_heads) return fail(PDK_ERR_SHAPE, "num_q_heads %d", Hq);
+  const ChunkedLayout L = chunked_layout(plan, Hq, Dv);
+  if (ws_bytes < L.total) return fail(PDK_ERR_WORKSPACE, "workspace %zu bytes < %zu", ws_bytes, L.total);
+  const int32_t* base = (const int32_t*)ws;
+  const auto& o = plan->off;
+  char* w = (char*)ws;
+  float* v_ch = chunk_out ? chunk_out : (float*)(w + L.v_ch);
+  float* l_ch = chunk_lse ? chunk_lse : (float*)(w + L.l_ch);
+  const int G = Hq / pre_pool->num_kv_heads;
+  const int B = plan->batch;
+  int st;
+  // chunk partials: each (request, chunk) is a view request with one member
+  if (plan->n_pre_parts > 0) {
+    pdk_csr vc{base + o.ch_indptr, base + o.ch_indices, base + o.ch_len, plan->n_chunks, 0};
+    st = partial_rows(pre_pool, &vc, q, q_dtype, Hq, sm_scale, plan->S, base + o.ch_parts,
+                      plan->n_pre_parts, base + o.ch_slots, base + o.ch_owner, 1, G,
+                      base + o.ch_parts, (float*)(w + L.v_pre), (float*)(w + L.l_pre), stream);
+    if (st) return st;
+  }
+  // each chunk's (O, LSE)
+  st = merge_rows((float*)(w + L.v_pre), (float*)(w + L.l_pre), plan->n_pre_parts, base + o.ch_parts,
+                  plan->n_chunks, Hq, Dv, v_ch, l_ch, 1, stream);
+  if (st) return st;
+  // across chunks -> even rows of the pair buffer
+  st = merge_rows(v_ch, l_ch, plan->n_chunks, base + o.req_chunks, B, Hq, Dv,
+                  (float*)(w + L.v_pair), (float*)(w + L.l_pair), 2, stream);
+  if (st) return st;
+  // suffix partials and their merge -> odd rows
+  if (plan->n_suf_parts > 0) {
+    pdk_csr vs{base + o.suf_indptr, base + o.suf_indices, base + o.suf_len, B, 0};
+    st = partial_rows(suf_pool, &vs, q, q_dtype, Hq, sm_scale, plan->Ss, base + o.suf_parts,
+                      plan->n_suf_parts, nullptr, nullptr, 0, G, base + o.suf_parts,
+                      (float*)(w + L.v_suf), (float*)(w + L.l_suf), stream);
+    if (st) return st;
+  }
+  st = merge_rows((float*)(w + L.v_suf), (float*)(w + L.l_suf), plan->n_suf_parts,
+                  base + o.suf_parts, B, Hq, Dv, (float*)(w + L.v_pair) + (size_t)Hq * Dv,
+                  (float*)(w + L.l_pair) + Hq, 2, stream);
+  if (st) return st;
+  // prefix state with suffix state
+  return merge_rows((float*)(w + L.v_pair), (float*)(w + L.l_pair), 2 * B, base + o.pair, B, Hq,
+                    Dv, out, lse_out, 1, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,110 @@
+"""Paged split-KV partials and flat decode on the GPU against the oracle
+[cascade-PR, "The decomposition" and "How the #898 merge kernel is reused"].
+
+Covers the tiny fp32 workload, the Llama-3-8B-shaped bf16 workload at a
+reduced batch (every partial, several tiles, ragged tails) and at its full
+size (sampled requests, the launch configuration the benchmark times),
+lengths around page and partition boundaries, empty requests, other head
+groupings (including more query rows per KV head than one workgroup keeps,
+which tiles the rows), and run-to-run determinism. Pools are NaN-poisoned
+outside every request's range, so a stray read fails the comparison."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import attention as oatt
+from gpu_util import TOL, assert_close, assert_lse, flat_decode, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def partials(pdk, batch, pool, csr, q, S=None):
+    S = batch.partition_tokens if S is None else S
+    pind = pdk.partition_indptr(batch.kv_len, S)
+    v, l = pdk.paged_decode_partial(pool, csr, q, batch.sm_scale, S,
+                                    torch.from_numpy(pind).cuda(), int(pind[-1]))
+    torch.cuda.synchronize()
+    return v.cpu().numpy(), l.cpu().numpy(), pind
+
+
+def check_partials_and_flat(pdk, batch, S=None):
+    pool, csr, q = to_device(batch)
+    v, l, pind = partials(pdk, batch, pool, csr, q, S)
+    rv, rl, rpind = oatt.partial_attention(batch, S)
+    assert np.array_equal(pind, rpind)
+    tol = TOL[batch.kv_dtype]
+    assert_close(v, rv, tol, "partial out")
+    assert_lse(l, rl, "partial lse")
+    out, lse, _ = flat_decode(batch, pool, csr, q, S)
+    ro, rlse = oatt.decode_attention(batch)
+    assert_close(out.cpu().numpy(), ro, tol, "flat out")
+    assert_lse(lse.cpu().numpy(), rlse, "flat lse")
+
+
+def test_tiny_gqa_fp32(gpu):
+    check_partials_and_flat(gpu, W.tiny_gqa_fp32())
+
+
+def test_llama3_shape_reduced_batch(gpu):
+    b = W.llama3_8b_flat(seed=2002, batch=6, min_len=100, max_len=1500)
+    check_partials_and_flat(gpu, b)
+
+
+@pytest.mark.parametrize("page_size,S", [(16, 512), (8, 64), (32, 96), (1, 16)])
+def test_lengths_around_boundaries(gpu, page_size, S):
+    lens = [1, page_size - 1 if page_size > 1 else 1, page_size, page_size + 1, S - 1, S, S + 1,
+            2 * S + 3, 0, 7]
+    b = W.random_batch(50 + page_size, batch=len(lens), page_size=page_size, num_q_heads=32,
+                       num_kv_heads=8, head_dim=128, kv_dtype="bf16", q_dtype="bf16",
+                       min_len=0, max_len=0, partition_tokens=S, lens=lens)
+    check_partials_and_flat(gpu, b)
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,kv,qd", [
+    (8, 8, 128, "bf16", "bf16"),     # G = 1
+    (16, 8, 128, "bf16", "bf16"),    # G = 2
+    (16, 2, 128, "bf16", "bf16"),    # G = 8
+    (32, 2, 64, "f32", "f32"),       # G = 16
+    (64, 2, 64, "bf16", "bf16"),     # G = 32: two row tiles per KV head
+    (12, 4, 64, "f32", "f32"),       # G = 3 (padded tile)
+    (8, 2, 256, "bf16", "bf16"),     # D = 256
+    (8, 2, 128, "bf16", "f32"),      # f32 queries on a bf16 pool
+    (8, 2, 64, "f32", "bf16"),       # bf16 queries on an f32 pool
+])
+def test_head_groupings_and_dtypes(gpu, Hq, Hkv, D, kv, qd):
+    b = W.random_batch(60 + Hq + D, batch=5, page_size=16, num_q_heads=Hq, num_kv_heads=Hkv,
+                       head_dim=D, kv_dtype=kv, q_dtype=qd, min_len=1, max_len=700,
+                       partition_tokens=128)
+    check_partials_and_flat(gpu, b)
+
+
+def test_latent_pool_value_aliases_key(gpu):
+    # one KV head, V = the key row itself (head_dim_v == head_dim_k here)
+    b = W.random_batch(71, batch=4, page_size=16, num_q_heads=8, num_kv_heads=1, head_dim=128,
+                       kv_dtype="bf16", q_dtype="bf16", min_len=1, max_len=300,
+                       partition_tokens=64, latent=True)
+    check_partials_and_flat(gpu, b)
+
+
+def test_llama3_full_size_sampled(gpu):
+    """The benchmark's flat launch: batch 64, lengths U[1024, 8192], 512-token
+    partitions. Checked on 6 sampled requests (all heads) and for finiteness
+    everywhere."""
+    b = W.llama3_8b_flat()
+    pool, csr, q = to_device(b)
+    out, lse, pind = flat_decode(b, pool, csr, q)
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    reqs = [0, 17, 33, int(np.argmax(b.kv_len)), int(np.argmin(b.kv_len)), 63]
+    ro, rl = oatt.decode_attention(b, requests=reqs)
+    assert_close(out[reqs], ro[reqs], TOL["bf16"], "flat out")
+    assert_lse(lse[reqs], rl[reqs], "flat lse")
+
+
+def test_deterministic(gpu):
+    b = W.llama3_8b_flat(seed=2003, batch=8, min_len=500, max_len=3000)
+    pool, csr, q = to_device(b)
+    o1, l1, _ = flat_decode(b, pool, csr, q)
+    o2, l2, _ = flat_decode(b, pool, csr, q)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
