@@ -3,13 +3,16 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload flat|cascade|merge|mla]
 
 A step is one attention layer's decode for the whole batch: every partial
-launch and every merge launch of the path. Inputs are seeded synthetic
-tensors already resident in HBM when the timed region starts. Prints one JSON
-line. ``value`` is achieved GB/s over the batch's unique KV bytes (the
-algorithmic bytes: each distinct page row read once); ``roofline`` reports the
-dominant kernel (the partial kernel) against the 8 TB/s HBM peak with its
-launch duration measured by HIP events on the launch stream; ``cpu_baseline``
-times the f64 oracle on a bounded sample on the host cores.
+launch and every merge of the path. Inputs are seeded synthetic tensors
+already resident in HBM when the timed region starts; plans (page-table
+bookkeeping on the host) are built and uploaded before it, as they are
+reused across a model's layers. Prints one JSON line.
+
+``value`` is the achieved rate over the batch's unique KV bytes (each
+distinct page row read once) per step; ``roofline`` reports the dominant
+kernel with its duration measured by HIP events on the stream it is launched
+on; ``cpu_baseline`` times the f64 oracle on a bounded sample of the same
+workload on the host cores.
 """
 from __future__ import annotations
 
@@ -47,115 +50,156 @@ def device_batch(torch, pdk, b, device):
     return pool, csr, dev_tensor(torch, b.q, device)
 
 
-class KernelTimer:
-    """HIP events around selected launches inside the timed steps."""
+class Timer:
+    """HIP events on the current stream around each step of the timed loop.
+
+    Every launch of the path is enqueued on the current (torch) stream, so
+    the events bracket exactly the kernels of the step."""
 
     def __init__(self, torch):
         self.torch = torch
-        self.pairs = {}
+        self.pairs = []
 
-    def wrap(self, name, fn):
+    def run(self, fn):
         s = self.torch.cuda.Event(enable_timing=True)
         e = self.torch.cuda.Event(enable_timing=True)
         s.record()
-        r = fn()
+        fn()
         e.record()
-        self.pairs.setdefault(name, []).append((s, e))
-        return r
+        self.pairs.append((s, e))
 
-    def mean_us(self, name):
-        ps = self.pairs.get(name, [])
-        if not ps:
-            return None
-        return 1000.0 * sum(s.elapsed_time(e) for s, e in ps) / len(ps)
-
-    def clear(self):
-        self.pairs = {}
+    def mean_us(self):
+        return 1000.0 * sum(s.elapsed_time(e) for s, e in self.pairs) / len(self.pairs)
 
 
-def timed_steps(torch, step, steps, warmup, timer):
+def time_steps(torch, step, steps, warmup):
+    """Wall time per step over exactly `steps` steps (synchronized on both
+    sides), plus the event-measured device time of each step."""
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    timer.clear()
+    timer = Timer(torch)
     t0 = time.perf_counter()
     for _ in range(steps):
-        step()
+        timer.run(step)
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) * 1000.0 / steps
+    wall_ms = (time.perf_counter() - t0) * 1000.0 / steps
+    return wall_ms, timer.mean_us()
 
 
-def cpu_baseline_flat(b, budget_s=15.0):
-    """The f64 oracle over a bounded sample of requests (whole requests, all
-    heads), reported in the same unit as the GPU value."""
+def cpu_baseline(batches, budget_s=15.0):
+    """The f64 oracle, whole requests with all heads, on a bounded sample:
+    GB of KV attended per second on one host thread."""
     import threadpoolctl
     from oracle import attention as oatt
-    order = np.random.default_rng(0).permutation(b.batch)
-    done, kv_bytes = [], 0
+    done, kv_bytes = 0, 0
     t0 = time.perf_counter()
     with threadpoolctl.threadpool_limits(1):
-        for r in order:
-            oatt.decode_attention(b, requests=[int(r)])
-            done.append(int(r))
-            kv_bytes += int(b.kv_len[r]) * b.kv_bytes_per_token()
-            if time.perf_counter() - t0 > budget_s:
-                break
+        for b in batches:
+            for r in np.random.default_rng(0).permutation(b.batch):
+                oatt.decode_attention(b, requests=[int(r)])
+                done += 1
+                kv_bytes += int(b.kv_len[r]) * b.kv_bytes_per_token()
+                if time.perf_counter() - t0 > budget_s:
+                    break
     dt = time.perf_counter() - t0
-    return {"value": kv_bytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(done)} of {b.batch} requests (all heads), f64 oracle, "
-                      f"1 thread, {dt:.1f} s"}
+    return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} requests of the same workload (all heads), f64 numpy oracle on "
+                      f"one thread, {dt:.1f} s"}
 
 
-def bench_flat(args, torch, pdk, W):
+def planned(torch, pdk, b, params, dev):
+    plan = pdk.CascadePlan(b.indptr, b.indices, b.kv_len, b.page_size, params)
+    t0 = time.perf_counter()
+    plan2 = pdk.CascadePlan(b.indptr, b.indices, b.kv_len, b.page_size, params)
+    plan_us = (time.perf_counter() - t0) * 1e6
+    del plan2
+    plan.upload(b.num_q_heads, b.head_dim_v, dev)
+    return plan, plan_us
+
+
+def run_plan_steps(args, torch, pdk, b, pool, q, plan, dev):
+    out = torch.empty((b.batch, b.num_q_heads, b.head_dim_v), dtype=torch.float32, device=dev)
+    lse = torch.empty((b.batch, b.num_q_heads), dtype=torch.float32, device=dev)
+    return time_steps(torch, lambda: plan.run(pool, q, b.sm_scale, out, lse), args.steps,
+                      args.warmup)
+
+
+def bench_flat(args, torch, pdk, W, dev):
     b = W.llama3_8b_flat()
-    dev = "cuda:0"
     pool, csr, q = device_batch(torch, pdk, b, dev)
     S = b.partition_tokens
-    pind = pdk.partition_indptr(b.kv_len, S)
-    R = int(pind[-1])
-    pind_d = torch.from_numpy(pind).to(dev)
+    plan, plan_us = planned(torch, pdk, b, pdk.CascadeParams(enabled=0, l1_partition_tokens=S), dev)
+    wall_ms, dev_us = run_plan_steps(args, torch, pdk, b, pool, q, plan, dev)
+    stats, _ = plan.stats()
+    R = stats["suffix_chunks"]
     Hq, Dv = b.num_q_heads, b.head_dim_v
-    v_part = torch.empty((R, Hq, Dv), dtype=torch.float32, device=dev)
-    lse_part = torch.empty((R, Hq), dtype=torch.float32, device=dev)
-    out = torch.empty((b.batch, Hq, Dv), dtype=torch.float32, device=dev)
-    lse = torch.empty((b.batch, Hq), dtype=torch.float32, device=dev)
-    timer = KernelTimer(torch)
-
-    def step():
-        timer.wrap("partial", lambda: pdk.paged_decode_partial(pool, csr, q, b.sm_scale, S, pind_d,
-                                                               R, v_part, lse_part))
-        timer.wrap("merge", lambda: pdk.merge_states(v_part, lse_part, pind_d, out, lse))
-
-    ms = timed_steps(torch, step, args.steps, args.warmup, timer)
-    t_part, t_merge = timer.mean_us("partial"), timer.mean_us("merge")
     kv = b.unique_kv_bytes()
-    q_bytes = b.q.nbytes
-    part_bytes = R * Hq * (Dv + 1) * 4
-    partial_alg = kv + q_bytes + part_bytes + b.indices.nbytes + b.kv_len.nbytes
-    value = kv / (ms * 1e-3) / 1e9
-    achieved = partial_alg / (t_part * 1e-6) / 1e9
+    # the one kernel of the step: KV read once, q, partial states written and
+    # read back by the fused merge, merged output written, page table
+    alg = (kv + b.q.nbytes + 2 * R * Hq * (Dv + 1) * 4 + b.batch * Hq * (Dv + 1) * 4
+           + b.indices.nbytes + b.kv_len.nbytes)
+    value = kv / (wall_ms * 1e-3) / 1e9
+    achieved = alg / (dev_us * 1e-6) / 1e9
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "llama3_8b_flat_decode", "batch": b.batch, "num_q_heads": Hq,
-                   "num_kv_heads": b.num_kv_heads, "head_dim": Dv, "page_size": b.page_size,
-                   "partition_tokens": S, "context": "uniform[1024,8192]",
-                   "total_tokens": int(b.kv_len.sum()), "partitions": R,
-                   "kv_dtype": "bf16", "parallelism": "none (1 GPU)"},
-        "us_per_step": round(ms * 1000, 2),
+        "config": {"workload": "llama3_8b_flat_paged_decode", "batch": b.batch,
+                   "num_q_heads": Hq, "num_kv_heads": b.num_kv_heads, "head_dim": Dv,
+                   "page_size": b.page_size, "partition_tokens": S,
+                   "context_tokens": "uniform[1024,8192]", "total_tokens": int(b.kv_len.sum()),
+                   "partitions": R, "kv_dtype": "bf16", "query_dtype": "bf16",
+                   "parallelism": "none (1 GPU)"},
+        "us_per_step": round(wall_ms * 1000, 2),
         "frac_of_peak": round(value / HBM_PEAK_GBS, 4),
         "unique_kv_bytes": kv,
-        "kernels_us": {"partial": round(t_part, 2), "merge": round(t_merge, 2)},
+        "plan_host_us": round(plan_us, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel": "partial_valu_kernel (bf16, D128, 4 rows)",
-                     "bytes_per_launch": partial_alg},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "partial_valu_kernel<bf16,bf16,D128,4 rows> with fused merge",
+                     "kernel_us": round(dev_us, 2), "bytes_per_launch": alg},
     }
+    batches = [b]
+    if not args.no_cascade:
+        res["cascade_vs_flat"] = bench_cascade_arms(args, torch, pdk, W, dev)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline_flat(b)
+        res["cpu_baseline"] = cpu_baseline(batches)
     return res
+
+
+def bench_cascade_arms(args, torch, pdk, W, dev):
+    """Shared-prefix workload (batch 72: 4 groups x 16 members sharing 4096
+    tokens, private suffixes U[64,1024], 8 non-members of 2048 tokens): flat,
+    the page's single-subgroup cascade, and every qualifying group."""
+    b = W.cascade_shared_prefix()
+    pool, csr, q = device_batch(torch, pdk, b, dev)
+    kv = b.unique_kv_bytes()
+    arms = {}
+    for name, params in (
+            ("flat", pdk.CascadeParams(enabled=0, l1_partition_tokens=512)),
+            ("cascade_single_group", pdk.CascadeParams(enabled=1, max_groups=1,
+                                                       l0_partition_tokens=256,
+                                                       l1_partition_tokens=512)),
+            ("cascade_all_groups", pdk.CascadeParams(enabled=1, max_groups=0,
+                                                     l0_partition_tokens=256,
+                                                     l1_partition_tokens=512))):
+        plan, plan_us = planned(torch, pdk, b, params, dev)
+        wall_ms, dev_us = run_plan_steps(args, torch, pdk, b, pool, q, plan, dev)
+        stats, decline = plan.stats()
+        arms[name] = {"us_per_step": round(wall_ms * 1000, 2), "device_us": round(dev_us, 2),
+                      "unique_kv_GBps": round(kv / (wall_ms * 1e-3) / 1e9, 2),
+                      "frac_of_peak": round(kv / (wall_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                      "plan_host_us": round(plan_us, 1), "members": stats["members"],
+                      "shared_pages": stats["shared_pages"], "decline": decline}
+        del plan
+    return {"workload": "cascade_shared_prefix_b72", "unique_kv_bytes": kv,
+            "flat_read_bytes": b.read_kv_bytes(), "arms": arms,
+            "speedup_all_groups": round(arms["flat"]["us_per_step"] /
+                                        arms["cascade_all_groups"]["us_per_step"], 3),
+            "speedup_single_group": round(arms["flat"]["us_per_step"] /
+                                          arms["cascade_single_group"]["us_per_step"], 3)}
 
 
 def main():
@@ -165,6 +209,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="flat", choices=["flat"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cascade", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share only; --gpus {args.gpus} is not supported "
@@ -177,7 +222,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     pdk.lib()
-    res = {"flat": bench_flat}[args.workload](args, torch, pdk, W)
+    res = {"flat": bench_flat}[args.workload](args, torch, pdk, W, "cuda:0")
     print(json.dumps(res), flush=True)
 
 

@@ -43,11 +43,13 @@ __device__ __forceinline__ void fp8x4_dequant_bf16(uint32_t w, float scale, uint
   p23 = pack_bf16x2_rne(f[2] * scale, f[3] * scale);
 }
 
-// DPP lane moves inside a row of 16 lanes.
+// DPP lane moves inside a row of 16 lanes. Every source lane exists for the
+// patterns below, so bound_ctrl is set and no "old" value is needed (the move
+// folds into the consuming VALU op as a DPP operand).
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
-                                                               CTRL, 0xF, 0xF, false));
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
 enum : int {
   DPP_QUAD_XOR1 = 0xB1,      // quad_perm [1,0,3,2]
@@ -63,6 +65,20 @@ __device__ __forceinline__ float row16_sum(float x) {
   x += dpp_f32<DPP_ROW_HALF_MIRROR>(x);
   x += dpp_f32<DPP_ROW_MIRROR>(x);
   return x;
+}
+
+// The same all-reduce over N independent values, one stage at a time, so
+// that consecutive DPP reads never wait on the VALU write before them.
+template <int N>
+__device__ __forceinline__ void row16_sum_n(float (&x)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] += dpp_f32<DPP_QUAD_XOR1>(x[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] += dpp_f32<DPP_QUAD_XOR2>(x[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] += dpp_f32<DPP_ROW_HALF_MIRROR>(x[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] += dpp_f32<DPP_ROW_MIRROR>(x[i]);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

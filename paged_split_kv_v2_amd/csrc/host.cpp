@@ -94,7 +94,8 @@ static int check_query(const void* q, int q_dtype, int Hq, const pdk_kv_pool* po
 int partial_rows(const pdk_kv_pool* pool, const pdk_csr* csr, const void* q, int q_dtype, int Hq,
                  float sm_scale, int S, const int* part_indptr, int num_parts,
                  const int* member_indptr, const int* members, int max_members, int G,
-                 const int* out_row_base, float* v_out, float* lse_out, hipStream_t stream) {
+                 const int* out_row_base, float* v_out, float* lse_out, hipStream_t stream,
+                 const int2* work) {
   int st = check_pool(pool);
   if (st) return st;
   if ((st = check_query(q, q_dtype, Hq, pool))) return st;
@@ -130,6 +131,7 @@ int partial_rows(const pdk_kv_pool* pool, const pdk_csr* csr, const void* q, int
   a.out_row_base = out_row_base;
   a.v_out = v_out;
   a.lse_out = lse_out;
+  a.work = work;
   return launch_partial(a, stream);
 }
 

@@ -50,6 +50,8 @@ struct PartialArgs {
   const int* out_row_base;    // flat: indexed by b; stacked: by member slot
   float* v_out;
   float* lse_out;
+  // planned launches: workgroup item i is (view request, partition) work[i]
+  const int2* work;           // nullptr: partition rows in part_indptr order
 };
 
 int launch_partial(const PartialArgs& a, hipStream_t stream);
@@ -62,10 +64,13 @@ int launch_merge(const float* v_in, const float* lse_in, int num_in, const int* 
 
 // Checked entry points used by the plan runners (same checks as the public
 // pdk_paged_decode_partial / pdk_merge_states, plus stacking and row maps).
+// work: optional longest-first (view request, partition) items, one per
+// partition of the view, that replace the part_indptr order.
 int partial_rows(const pdk_kv_pool* pool, const pdk_csr* view, const void* q, int q_dtype, int Hq,
                  float sm_scale, int S, const int* part_indptr, int num_parts,
                  const int* member_indptr, const int* members, int max_members, int G,
-                 const int* out_row_base, float* v_out, float* lse_out, hipStream_t stream);
+                 const int* out_row_base, float* v_out, float* lse_out, hipStream_t stream,
+                 const int2* work = nullptr);
 int merge_rows(const float* v_in, const float* lse_in, int num_in, const int* o_indptr,
                int num_out, int H, int D, float* v_out, float* lse_out, int out_stride,
                hipStream_t stream);

@@ -8,9 +8,9 @@
 //
 // The merge is a pure stream (about 2 flops per loaded element), so it is
 // laid out for HBM: each thread owns four consecutive floats of one output
-// row (one 16-byte load per input row), a workgroup covers 1024 floats of
-// the [H, D] row, and the group's input rows are read four at a time so that
-// several independent 16-byte loads per thread are in flight.
+// row (one 16-byte load per input row), a one-wave workgroup covers 256
+// floats of the [H, D] row, and a group's input rows are read eight at a
+// time so that eight independent 16-byte loads per thread are in flight.
 
 #include "device.h"
 #include "internal.h"
@@ -19,8 +19,9 @@ namespace pdk {
 
 namespace {
 
-constexpr int kMergeThreads = 256;
-constexpr int kMergeSpan = kMergeThreads * 4;  // floats per workgroup
+constexpr int kMergeThreads = 64;              // one wave per workgroup
+constexpr int kMergeSpan = kMergeThreads * 4;  // floats of an output row per workgroup
+constexpr int kMergeBatch = 8;                 // input rows whose loads are issued together
 
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
     const float* __restrict__ v_in, const float* __restrict__ lse_in, int num_in,
@@ -39,13 +40,13 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
 
   float4 out = make_float4(0.f, 0.f, 0.f, 0.f);
   float lse = -INFINITY;
-  const float lse0 = n > 0 ? lse_in[(size_t)a * H + head] : -INFINITY;
+  const float* lrow = lse_in + (size_t)a * H + head;
+  const float lse0 = n > 0 ? lrow[0] : -INFINITY;
   if (n == 1 && lse0 != -INFINITY) {
     // identity, bit for bit
     out = *reinterpret_cast<const float4*>(v_in + (size_t)a * HD + e);
     lse = lse0;
   } else if (n > 1) {
-    const float* lrow = lse_in + (size_t)a * H + head;
     float m = -INFINITY;
     for (int r = 0; r < n; ++r) m = fmaxf(m, lrow[(size_t)r * H]);
     if (m != -INFINITY) {
@@ -53,38 +54,25 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
       float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
       const float4* vrow = reinterpret_cast<const float4*>(v_in + (size_t)a * HD + e);
       const size_t vstep = (size_t)HD / 4;
-      int r = 0;
-      for (; r + 4 <= n; r += 4) {
-        float w[4];
-        float4 x[4];
+      for (int r0 = 0; r0 < n; r0 += kMergeBatch) {
+        float w[kMergeBatch];
+        float4 x[kMergeBatch];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          w[k] = lrow[(size_t)(r + k) * H];
-          x[k] = vrow[(size_t)(r + k) * vstep];
+        for (int k = 0; k < kMergeBatch; ++k) {
+          const bool in = r0 + k < n;
+          w[k] = in ? lrow[(size_t)(r0 + k) * H] : -INFINITY;
+          x[k] = in ? vrow[(size_t)(r0 + k) * vstep] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const bool live = w[k] != -INFINITY;
-          const float wk = live ? fast_exp2(w[k] - m) : 0.f;
+        for (int k = 0; k < kMergeBatch; ++k) {
+          if (w[k] == -INFINITY) continue;  // empty state: not read into the sum
+          const float wk = fast_exp2(w[k] - m);
           l += wk;
-          if (live) {
-            acc.x = fmaf(wk, x[k].x, acc.x);
-            acc.y = fmaf(wk, x[k].y, acc.y);
-            acc.z = fmaf(wk, x[k].z, acc.z);
-            acc.w = fmaf(wk, x[k].w, acc.w);
-          }
+          acc.x = fmaf(wk, x[k].x, acc.x);
+          acc.y = fmaf(wk, x[k].y, acc.y);
+          acc.z = fmaf(wk, x[k].z, acc.z);
+          acc.w = fmaf(wk, x[k].w, acc.w);
         }
-      }
-      for (; r < n; ++r) {
-        const float lr = lrow[(size_t)r * H];
-        if (lr == -INFINITY) continue;
-        const float4 x = vrow[(size_t)r * vstep];
-        const float wk = fast_exp2(lr - m);
-        l += wk;
-        acc.x = fmaf(wk, x.x, acc.x);
-        acc.y = fmaf(wk, x.y, acc.y);
-        acc.z = fmaf(wk, x.z, acc.z);
-        acc.w = fmaf(wk, x.w, acc.w);
       }
       out = make_float4(acc.x / l, acc.y / l, acc.z / l, acc.w / l);
       lse = m + log2f(l);

@@ -10,16 +10,23 @@
 // partial is normalized by its own denominator and its LSE is m + log2 l].
 //
 // Layout of the work inside a workgroup (256 threads = 4 waves):
+//   * the partition's page ids are staged once in LDS, so no K/V address
+//     waits on a global load inside the loop;
 //   * a "row group" is one DPP row of 16 lanes; it owns one token at a time,
 //     lane j holding elements [j*E, (j+1)*E) of the K and V rows (E = D/16),
-//     fetched with one or two 8/16-byte loads per row - a row group reads a
-//     contiguous K row, a wave reads four adjacent tokens of a page;
+//     fetched with 8- or 16-byte loads - a row group reads a contiguous K
+//     row, a wave reads four adjacent tokens of a page;
 //   * each step, the 16 row groups take 4 tokens each: token
-//     t0 + u*16 + rowgroup, u = 0..3, i.e. 64 consecutive tokens;
+//     t0 + u*16 + rowgroup, u = 0..3, i.e. 64 consecutive tokens; the K/V
+//     rows of step i+1 are requested before step i is computed, so each lane
+//     keeps 16 loads in flight;
+//   * tokens past the end of the range are clamped to the last valid token
+//     (a valid, finite row) and masked to score -inf, so the loop has no
+//     per-token branches;
 //   * each lane keeps the running (max, sum, accumulator) of every owned
 //     query row for the tokens its row group has seen (online softmax in
 //     log2 units); the K/V elements it loaded are reused from registers for
-//     every owned query row, so nothing is staged through LDS in the loop;
+//     every owned query row;
 //   * q.k partial dots are summed across the row group with DPP
 //     (quad_perm, row_half_mirror, row_mirror) - no LDS traffic;
 //   * at the end the 16 row-group states are merged exactly (cross-row
@@ -37,25 +44,33 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kRowGroups = kThreads / 16;
-constexpr int kTokPerRowGroup = 4;
-constexpr int kStepTokens = kRowGroups * kTokPerRowGroup;  // 64
+// tokens each row group takes per step: 4, or 2 when many query rows leave
+// few registers for the two K/V tiles
+template <int GM, int E>
+struct TokPerRowGroup { static constexpr int value = (GM * E >= 64 && GM >= 8) ? 2 : 4; };
+constexpr int kMaxPartPages = 1024;                         // page ids staged in LDS
+constexpr float kLazyLog2 = 8.f;  // headroom of the lazily raised softmax maximum
 
 enum { KV_F32 = 0, KV_BF16 = 1 };
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// K/V rows are read exactly once: non-temporal (streaming) loads.
 template <int NU>
 __device__ __forceinline__ void load_words(const uint32_t* __restrict__ p, uint32_t (&w)[NU]) {
   if constexpr (NU % 4 == 0) {
 #pragma unroll
     for (int i = 0; i < NU / 4; ++i) {
-      uint4 x = reinterpret_cast<const uint4*>(p)[i];
-      w[4 * i] = x.x; w[4 * i + 1] = x.y; w[4 * i + 2] = x.z; w[4 * i + 3] = x.w;
+      const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p) + i);
+      w[4 * i] = x[0]; w[4 * i + 1] = x[1]; w[4 * i + 2] = x[2]; w[4 * i + 3] = x[3];
     }
   } else if constexpr (NU == 2) {
-    uint2 x = *reinterpret_cast<const uint2*>(p);
-    w[0] = x.x; w[1] = x.y;
+    const u32x2_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+    w[0] = x[0]; w[1] = x[1];
   } else {
 #pragma unroll
-    for (int i = 0; i < NU; ++i) w[i] = p[i];
+    for (int i = 0; i < NU; ++i) w[i] = __builtin_nontemporal_load(p + i);
   }
 }
 
@@ -74,16 +89,27 @@ __device__ __forceinline__ void widen(const uint32_t (&w)[NU], float (&f)[E]) {
   }
 }
 
-template <int KT, int QT, int D, int GM>
+template <int NU, int T>
+struct Tile {
+  uint32_t kw[T][NU];
+  uint32_t vw[T][NU];
+  bool valid[T];
+};
+
+template <int KT, int QT, int D, int GM, bool UNIF>
 __global__ __launch_bounds__(kThreads) void partial_valu_kernel(const PartialArgs a) {
   constexpr int E = D / 16;                          // elements per lane
   constexpr int NU = E * (KT == KV_F32 ? 4 : 2) / 4; // 32-bit words per lane per row
   constexpr bool kDot2 = (KT == KV_BF16 && QT == PDK_BF16);
   constexpr int QW = kDot2 ? E / 2 : E;              // per-row query registers
+  constexpr int ESZ = (KT == KV_F32) ? 4 : 2;
+  constexpr int T = TokPerRowGroup<GM, E>::value;
+  constexpr int kStep = 16 * T;  // tokens per step of the workgroup
 
   __shared__ float sm_acc[4][GM][D];
   __shared__ float sm_m[4][GM];
   __shared__ float sm_l[4][GM];
+  __shared__ int sm_pid[kMaxPartPages];
 
   const int n_tiles = (a.max_rows + GM - 1) / GM;
   int bid = blockIdx.x;
@@ -92,14 +118,24 @@ __global__ __launch_bounds__(kThreads) void partial_valu_kernel(const PartialArg
   const int h = bid % a.Hkv;
   const int r = bid / a.Hkv;
 
-  // request of partition row r: the largest b with part_indptr[b] <= r
-  int lo = 0, hi = a.batch;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.part_indptr[mid] <= r) lo = mid; else hi = mid;
+  const int tid = threadIdx.x;
+  int b = 0, p;
+  if (a.work != nullptr) {
+    // planned launch: item r of the (longest-first) work list
+    const int2 it = a.work[r];
+    b = it.x;
+    p = it.y;
+  } else {
+    // request of partition row r: the largest b with part_indptr[b] <= r,
+    // i.e. the number of b in [1, batch) with part_indptr[b] <= r (monotone);
+    // each wave counts 64 candidates per load with a ballot
+    for (int base = 1; base < a.batch; base += 64) {
+      const int i = base + (tid & 63);
+      const bool le = (i < a.batch) && (a.part_indptr[i] <= r);
+      b += __popcll(__ballot(le));
+    }
+    p = r - a.part_indptr[b];
   }
-  const int b = lo;
-  const int p = r - a.part_indptr[b];
 
   const bool stacked = a.member_indptr != nullptr;
   const int mbase = stacked ? a.member_indptr[b] : 0;
@@ -112,10 +148,20 @@ __global__ __launch_bounds__(kThreads) void partial_valu_kernel(const PartialArg
   const int start = p * a.S;
   int end = min(start + a.S, a.kv_len[b]);
   end = min(end, npages * a.P);
+  const int shift = a.p_shift;  // page size is a power of two on this path
 
-  const int tid = threadIdx.x;
   const int rg = tid >> 4;
   const int j = tid & 15;
+
+  // stage the partition's page ids (-1 marks an id outside the pool)
+  const int pg_first = start >> shift;
+  if (end > start) {
+    const int n_pg = ((end - 1) >> shift) - pg_first + 1;
+    for (int i = tid; i < n_pg; i += kThreads) {
+      const int pid = a.indices[page0 + pg_first + i];
+      sm_pid[i] = ((unsigned)pid < (unsigned)a.num_blocks) ? pid : -1;
+    }
+  }
 
   // queries of the owned rows (zero for rows past nrows)
   uint32_t qw[GM][QW];
@@ -146,6 +192,8 @@ __global__ __launch_bounds__(kThreads) void partial_valu_kernel(const PartialArg
     }
   }
 
+  // running state; run_m is a reference maximum that is only raised when a
+  // score exceeds it by more than kLazyLog2, so weights stay <= 2^kLazyLog2
   float run_m[GM], run_l[GM], acc[GM][E];
 #pragma unroll
   for (int gi = 0; gi < GM; ++gi) {
@@ -155,50 +203,43 @@ __global__ __launch_bounds__(kThreads) void partial_valu_kernel(const PartialArg
     for (int e = 0; e < E; ++e) acc[gi][e] = 0.f;
   }
 
-  const int esz = (KT == KV_F32) ? 4 : 2;
-  const char* kbase = reinterpret_cast<const char*>(a.k) + (size_t)h * a.k_hstride * esz;
+  const char* kbase = reinterpret_cast<const char*>(a.k) + (size_t)h * a.k_hstride * ESZ;
   const bool latent = a.v == nullptr;
   const char* vbase = latent ? kbase
-                             : reinterpret_cast<const char*>(a.v) + (size_t)h * a.v_hstride * esz;
-  const long long kb_stride = a.k_bstride * esz, vb_stride = (latent ? a.k_bstride : a.v_bstride) * esz;
-  const int krow = a.Dk * esz, vrow = (latent ? a.Dk : a.Dv) * esz;
+                             : reinterpret_cast<const char*>(a.v) + (size_t)h * a.v_hstride * ESZ;
+  const long long kb_stride = a.k_bstride * ESZ;
+  const long long vb_stride = (latent ? a.k_bstride : a.v_bstride) * ESZ;
+  const uint32_t krow = a.Dk * ESZ, vrow = (latent ? a.Dk : a.Dv) * ESZ;
+  const uint32_t lane_off = j * NU * 4;
+  const int pmask = a.P - 1;
+  __syncthreads();  // page ids visible
 
-  for (int t0 = start; t0 < end; t0 += kStepTokens) {
-    uint32_t kw[kTokPerRowGroup][NU], vw[kTokPerRowGroup][NU];
-    bool valid[kTokPerRowGroup];
+  auto load_step = [&](int t0, Tile<NU, T>& X) {
 #pragma unroll
-    for (int u = 0; u < kTokPerRowGroup; ++u) {
+    for (int u = 0; u < T; ++u) {
       const int t = t0 + u * 16 + rg;
-      int pid = -1, slot = 0;
-      if (t < end) {
-        int pg;
-        if (a.p_shift >= 0) { pg = t >> a.p_shift; slot = t & (a.P - 1); }
-        else { pg = t / a.P; slot = t - pg * a.P; }
-        pid = a.indices[page0 + pg];
-      }
-      valid[u] = (t < end) && (unsigned)pid < (unsigned)a.num_blocks;
-      if (valid[u]) {
-        load_words<NU>(reinterpret_cast<const uint32_t*>(kbase + pid * kb_stride + slot * krow) + j * NU,
-                       kw[u]);
-        if (latent) {
-#pragma unroll
-          for (int i = 0; i < NU; ++i) vw[u][i] = kw[u][i];
-        } else {
-          load_words<NU>(reinterpret_cast<const uint32_t*>(vbase + pid * vb_stride + slot * vrow) + j * NU,
-                         vw[u]);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < NU; ++i) { kw[u][i] = 0; vw[u][i] = 0; }
-      }
+      const int tc = min(t, end - 1);
+      int pid = sm_pid[(tc >> shift) - pg_first];
+      // with pages of >= 16 tokens, the 4 tokens a wave takes for one u lie
+      // in one page: its row base is wave-uniform (scalar address)
+      if constexpr (UNIF) pid = __builtin_amdgcn_readfirstlane(pid);
+      X.valid[u] = (t < end) && (pid >= 0);
+      pid = max(pid, 0);
+      const uint32_t slot = (uint32_t)(tc & pmask);
+      const char* kp = kbase + pid * kb_stride;
+      const char* vp = vbase + pid * vb_stride;
+      load_words<NU>(reinterpret_cast<const uint32_t*>(kp + (slot * krow + lane_off)), X.kw[u]);
+      load_words<NU>(reinterpret_cast<const uint32_t*>(vp + (slot * vrow + lane_off)), X.vw[u]);
     }
+  };
 
-    // scores s[u][gi] in log2 units
-    float s[kTokPerRowGroup][GM];
+  auto compute_step = [&](const Tile<NU, T>& X) {
+    // q.k partial dots, summed over the row group one DPP stage at a time
+    float s[T * GM];
 #pragma unroll
-    for (int u = 0; u < kTokPerRowGroup; ++u) {
+    for (int u = 0; u < T; ++u) {
       float kf[E];
-      if constexpr (!kDot2) widen<KT, E, NU>(kw[u], kf);
+      if constexpr (!kDot2) widen<KT, E, NU>(X.kw[u], kf);
 #pragma unroll
       for (int gi = 0; gi < GM; ++gi) {
         float d = 0.f;
@@ -206,45 +247,94 @@ __global__ __launch_bounds__(kThreads) void partial_valu_kernel(const PartialArg
 #pragma unroll
           for (int i = 0; i < QW; ++i)
             d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qw[gi][i]),
-                                                __builtin_bit_cast(bf16x2_t, kw[u][i]), d, false);
+                                                __builtin_bit_cast(bf16x2_t, X.kw[u][i]), d,
+                                                false);
         } else {
 #pragma unroll
           for (int e = 0; e < E; ++e) d = fmaf(bits_f32(qw[gi][e]), kf[e], d);
         }
-        d = row16_sum(d);
-        s[u][gi] = valid[u] ? d * a.scale_log2 : -INFINITY;
+        s[u * GM + gi] = d;
       }
     }
-
-    float vf[kTokPerRowGroup][E];
+    row16_sum_n<T * GM>(s);
 #pragma unroll
-    for (int u = 0; u < kTokPerRowGroup; ++u) widen<KT, E, NU>(vw[u], vf[u]);
+    for (int u = 0; u < T; ++u)
+#pragma unroll
+      for (int gi = 0; gi < GM; ++gi)
+        s[u * GM + gi] = X.valid[u] ? s[u * GM + gi] * a.scale_log2 : -INFINITY;
 
+    // raise the reference maxima only where a score jumped past them
+    float mx[GM];
+    int need = 0;
 #pragma unroll
     for (int gi = 0; gi < GM; ++gi) {
-      float mx = s[0][gi];
+      mx[gi] = s[gi];
 #pragma unroll
-      for (int u = 1; u < kTokPerRowGroup; ++u) mx = fmaxf(mx, s[u][gi]);
-      const float mn = fmaxf(run_m[gi], mx);
-      const float mu = (mn == -INFINITY) ? 0.f : mn;
-      const float corr = fast_exp2(run_m[gi] - mu);
-      float pu[kTokPerRowGroup];
-      float psum = 0.f;
+      for (int u = 1; u < T; ++u) mx[gi] = fmaxf(mx[gi], s[u * GM + gi]);
+      need |= mx[gi] > run_m[gi] + kLazyLog2;
+    }
+    if (__any(need)) {
 #pragma unroll
-      for (int u = 0; u < kTokPerRowGroup; ++u) {
-        pu[u] = fast_exp2(s[u][gi] - mu);
-        psum += pu[u];
-      }
-      run_l[gi] = run_l[gi] * corr + psum;
-      run_m[gi] = mn;
+      for (int gi = 0; gi < GM; ++gi) {
+        const float mn = (mx[gi] > run_m[gi] + kLazyLog2) ? mx[gi] : run_m[gi];
+        const float corr = (mn == run_m[gi]) ? 1.f : fast_exp2(run_m[gi] - mn);
+        run_l[gi] *= corr;
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        float x = acc[gi][e] * corr;
-#pragma unroll
-        for (int u = 0; u < kTokPerRowGroup; ++u) x = fmaf(pu[u], vf[u][e], x);
-        acc[gi][e] = x;
+        for (int e = 0; e < E; ++e) acc[gi][e] *= corr;
+        run_m[gi] = mn;
       }
     }
+#pragma unroll
+    for (int gi = 0; gi < GM; ++gi) {
+      const float mu = (run_m[gi] == -INFINITY) ? 0.f : run_m[gi];
+      float psum = 0.f;
+#pragma unroll
+      for (int u = 0; u < T; ++u) {
+        s[u * GM + gi] = fast_exp2(s[u * GM + gi] - mu);
+        psum += s[u * GM + gi];
+      }
+      run_l[gi] += psum;
+    }
+    // acc += p * v, widening each stored pair of V just before its use
+#pragma unroll
+    for (int u = 0; u < T; ++u) {
+      if constexpr (KT == KV_F32) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float v = bits_f32(X.vw[u][e]);
+#pragma unroll
+          for (int gi = 0; gi < GM; ++gi) acc[gi][e] = fmaf(s[u * GM + gi], v, acc[gi][e]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < E / 2; ++i) {
+          const float v0 = bf16_lo(X.vw[u][i]), v1 = bf16_hi(X.vw[u][i]);
+#pragma unroll
+          for (int gi = 0; gi < GM; ++gi) {
+            acc[gi][2 * i] = fmaf(s[u * GM + gi], v0, acc[gi][2 * i]);
+            acc[gi][2 * i + 1] = fmaf(s[u * GM + gi], v1, acc[gi][2 * i + 1]);
+          }
+        }
+      }
+    }
+  };
+
+  // two register tiles: the next step's rows are requested before the
+  // current step is computed
+  Tile<NU, T> A, B;
+  int t0 = start;
+  if (t0 < end) load_step(t0, A);
+  while (t0 < end) {
+    const bool more1 = t0 + kStep < end;  // uniform
+    if (more1) load_step(t0 + kStep, B);
+    compute_step(A);
+    t0 += kStep;
+    if (!more1) break;
+    const bool more2 = t0 + kStep < end;
+    if (more2) load_step(t0 + kStep, A);
+    compute_step(B);
+    t0 += kStep;
+    if (!more2) break;
   }
 
   // merge the four row groups of this wave (lanes l, l^16, l^32, l^48)
@@ -303,25 +393,25 @@ __global__ __launch_bounds__(kThreads) void partial_valu_kernel(const PartialArg
 
 typedef void (*KernelFn)(const PartialArgs);
 
-template <int KT, int QT, int D>
+template <int KT, int QT, int D, bool U>
 KernelFn pick_gm(int gm) {
   constexpr int E = D / 16;
   switch (gm) {
-    case 1: return partial_valu_kernel<KT, QT, D, 1>;
-    case 2: return partial_valu_kernel<KT, QT, D, 2>;
-    case 4: return partial_valu_kernel<KT, QT, D, 4>;
-    case 8: if constexpr (8 * E <= 128) return partial_valu_kernel<KT, QT, D, 8>; else return nullptr;
-    case 16: if constexpr (16 * E <= 128) return partial_valu_kernel<KT, QT, D, 16>; else return nullptr;
+    case 1: return partial_valu_kernel<KT, QT, D, 1, U>;
+    case 2: return partial_valu_kernel<KT, QT, D, 2, U>;
+    case 4: return partial_valu_kernel<KT, QT, D, 4, U>;
+    case 8: if constexpr (8 * E <= 128) return partial_valu_kernel<KT, QT, D, 8, U>; else return nullptr;
+    case 16: if constexpr (16 * E <= 128) return partial_valu_kernel<KT, QT, D, 16, U>; else return nullptr;
   }
   return nullptr;
 }
 
 template <int KT, int QT>
-KernelFn pick_d(int d, int gm) {
+KernelFn pick_d(int d, int gm, bool unif) {
   switch (d) {
-    case 64: return pick_gm<KT, QT, 64>(gm);
-    case 128: return pick_gm<KT, QT, 128>(gm);
-    case 256: return pick_gm<KT, QT, 256>(gm);
+    case 64: return unif ? pick_gm<KT, QT, 64, true>(gm) : pick_gm<KT, QT, 64, false>(gm);
+    case 128: return unif ? pick_gm<KT, QT, 128, true>(gm) : pick_gm<KT, QT, 128, false>(gm);
+    case 256: return unif ? pick_gm<KT, QT, 256, true>(gm) : pick_gm<KT, QT, 256, false>(gm);
   }
   return nullptr;
 }
@@ -335,14 +425,20 @@ int launch_partial_valu(const PartialArgs& a, hipStream_t stream) {
   if (a.Dk != a.Dv)
     return fail(PDK_ERR_UNSUPPORTED, "vector path needs head_dim_k == head_dim_v (got %d, %d)",
                 a.Dk, a.Dv);
+  if (a.p_shift < 0)
+    return fail(PDK_ERR_UNSUPPORTED, "vector path needs a power-of-two page size (got %d)", a.P);
+  if (a.S / a.P + 1 > kMaxPartPages)
+    return fail(PDK_ERR_UNSUPPORTED, "partition of %d tokens spans more than %d pages", a.S,
+                kMaxPartPages - 1);
   int gm = 1;
   while (gm < a.max_rows && gm < valu_max_rows(a.Dk)) gm <<= 1;
   KernelFn fn = nullptr;
   const int kt = a.kv_dtype, qt = a.q_dtype;
-  if (kt == PDK_F32 && qt == PDK_F32) fn = pick_d<KV_F32, PDK_F32>(a.Dk, gm);
-  else if (kt == PDK_F32 && qt == PDK_BF16) fn = pick_d<KV_F32, PDK_BF16>(a.Dk, gm);
-  else if (kt == PDK_BF16 && qt == PDK_F32) fn = pick_d<KV_BF16, PDK_F32>(a.Dk, gm);
-  else if (kt == PDK_BF16 && qt == PDK_BF16) fn = pick_d<KV_BF16, PDK_BF16>(a.Dk, gm);
+  const bool unif = a.P >= 16;  // a wave's four tokens of one step share a page
+  if (kt == PDK_F32 && qt == PDK_F32) fn = pick_d<KV_F32, PDK_F32>(a.Dk, gm, unif);
+  else if (kt == PDK_F32 && qt == PDK_BF16) fn = pick_d<KV_F32, PDK_BF16>(a.Dk, gm, unif);
+  else if (kt == PDK_BF16 && qt == PDK_F32) fn = pick_d<KV_BF16, PDK_F32>(a.Dk, gm, unif);
+  else if (kt == PDK_BF16 && qt == PDK_BF16) fn = pick_d<KV_BF16, PDK_BF16>(a.Dk, gm, unif);
   if (!fn)
     return fail(PDK_ERR_UNSUPPORTED,
                 "no vector kernel for kv dtype %d, q dtype %d, head dim %d, %d rows", kt, qt,

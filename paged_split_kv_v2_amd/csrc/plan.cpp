@@ -68,6 +68,26 @@ struct Candidate {
   int32_t reason;
 };
 
+// (view request, partition) pairs of a view, flattened as int pairs, ordered
+// by partition length (descending), then request and partition (ascending).
+std::vector<int32_t> longest_first(const std::vector<int32_t>& part_indptr,
+                                   const std::vector<int32_t>& len, int S) {
+  struct Item { int32_t b, p, n; };
+  std::vector<Item> items;
+  for (size_t b = 0; b + 1 < part_indptr.size(); ++b)
+    for (int p = 0; p < part_indptr[b + 1] - part_indptr[b]; ++p)
+      items.push_back({(int32_t)b, p, std::max(0, std::min(S, len[b] - p * S))});
+  std::stable_sort(items.begin(), items.end(),
+                   [](const Item& x, const Item& y) { return x.n > y.n; });
+  std::vector<int32_t> out;
+  out.reserve(items.size() * 2);
+  for (const auto& it : items) {
+    out.push_back(it.b);
+    out.push_back(it.p);
+  }
+  return out;
+}
+
 }  // namespace
 
 struct pdk_cascade_plan {
@@ -83,6 +103,7 @@ struct pdk_cascade_plan {
   struct {
     size_t l0_indptr, l0_indices, l0_len, l0_parts, group_indptr, members, member_rows;
     size_t l1_indptr, l1_indices, l1_len, l1_parts, l1_rows, fused;
+    size_t l0_work, l1_work;
   } off{};
   const void* uploaded_to = nullptr;
 };
@@ -221,9 +242,12 @@ int pdk_cascade_plan_create(const pdk_csr* csr, int32_t P, const pdk_cascade_par
   plan->l0_part_indptr.assign(1, 0);
   for (int k = 0; k < K; ++k)
     plan->l0_part_indptr.push_back(plan->l0_part_indptr.back() + ceil_div(F[PDK_PLAN_L0_LEN][k], S0));
+  // every request owns at least one level-1 row: an empty range is the
+  // state (0, -inf), so its merged output is still written
   plan->l1_part_indptr.assign(1, 0);
   for (int b = 0; b < B; ++b)
-    plan->l1_part_indptr.push_back(plan->l1_part_indptr.back() + ceil_div(F[PDK_PLAN_L1_LEN][b], S1));
+    plan->l1_part_indptr.push_back(plan->l1_part_indptr.back() +
+                                   std::max(1, ceil_div(F[PDK_PLAN_L1_LEN][b], S1)));
   plan->n_l0_parts = plan->l0_part_indptr.back();
   plan->n_l1_parts = plan->l1_part_indptr.back();
   auto& fused = F[PDK_PLAN_FUSED_MERGE_INDPTR];
@@ -270,6 +294,10 @@ int pdk_cascade_plan_create(const pdk_csr* csr, int32_t P, const pdk_cascade_par
   plan->off.l1_parts = bl.add(plan->l1_part_indptr);
   plan->off.l1_rows = bl.add(plan->l1_row_base);
   plan->off.fused = bl.add(fused);
+  // work lists, longest partition first: the hardware dispatcher hands out
+  // workgroups in order, so the short tail partitions fill the last gaps
+  plan->off.l0_work = bl.add(longest_first(plan->l0_part_indptr, F[PDK_PLAN_L0_LEN], S0));
+  plan->off.l1_work = bl.add(longest_first(plan->l1_part_indptr, F[PDK_PLAN_L1_LEN], S1));
   *plan_out = plan;
   return PDK_OK;
 }
@@ -332,25 +360,24 @@ int pdk_run_cascade_decode(const pdk_cascade_plan* plan, const pdk_kv_pool* pool
   float* lse_part = (float*)((char*)v_part + align256((size_t)plan->total_rows * Hq * pool->head_dim_v * 4));
   const int G = Hq / pool->num_kv_heads;
 
-  // level 1: every request's remaining range (the flat batch when declined)
-  if (plan->n_l1_parts > 0) {
-    pdk_csr v1{base + o.l1_indptr, base + o.l1_indices, base + o.l1_len, plan->batch, 0};
-    int st = partial_rows(pool, &v1, q, q_dtype, Hq, sm_scale,
-                                           plan->params.l1_partition_tokens, base + o.l1_parts,
-                                           plan->n_l1_parts, nullptr, nullptr, 0, G,
-                                           base + o.l1_rows, v_part, lse_part, stream);
-    if (st) return st;
-  }
-  // level 0: each selected group's span once, members stacked KV-head-major
+  // level 0: each selected group's span once, members stacked KV-head-major,
+  // partials written straight into the members' rows
   if (plan->n_l0_parts > 0) {
     pdk_csr v0{base + o.l0_indptr, base + o.l0_indices, base + o.l0_len, plan->n_groups, 0};
-    int st = partial_rows(pool, &v0, q, q_dtype, Hq, sm_scale,
-                                           plan->params.l0_partition_tokens, base + o.l0_parts,
-                                           plan->n_l0_parts, base + o.group_indptr,
-                                           base + o.members, plan->max_members, G,
-                                           base + o.member_rows, v_part, lse_part, stream);
+    int st = partial_rows(pool, &v0, q, q_dtype, Hq, sm_scale, plan->params.l0_partition_tokens,
+                          base + o.l0_parts, plan->n_l0_parts, base + o.group_indptr,
+                          base + o.members, plan->max_members, G, base + o.member_rows, v_part,
+                          lse_part, stream, reinterpret_cast<const int2*>(base + o.l0_work));
     if (st) return st;
   }
+  // level 1: every request's remaining range (the flat batch when declined)
+  pdk_csr v1{base + o.l1_indptr, base + o.l1_indices, base + o.l1_len, plan->batch, 0};
+  int st = partial_rows(pool, &v1, q, q_dtype, Hq, sm_scale, plan->params.l1_partition_tokens,
+                        base + o.l1_parts, plan->n_l1_parts, nullptr, nullptr, 0, G,
+                        base + o.l1_rows, v_part, lse_part, stream,
+                        reinterpret_cast<const int2*>(base + o.l1_work));
+  if (st) return st;
+  // one merge per request over its [level-0][level-1] rows
   return pdk_merge_states(v_part, lse_part, plan->total_rows, base + o.fused, plan->batch, Hq,
                           pool->head_dim_v, out, lse_out, stream);
 }

@@ -178,3 +178,31 @@ def test_member_major_stacking_reads_the_wrong_kv_head(gpu):
     member_major = want.reshape(M * Hq, 64)   # row m*Hq + i is member m's head i
     assert rel_err(res["kv_major"], kv_major) <= 1e-5
     assert rel_err(res["member_major"], member_major) > 1e-2
+
+
+def test_plan_runs_repeat_and_cover_empty_requests(gpu):
+    """Planned runs merge inside the level-1 launch (last workgroup per
+    request and KV head); counters must return to zero so that repeated runs
+    agree bit for bit, and an empty request still gets (0, -inf)."""
+    lens = [300, 0, 530, 530, 17, 0, 530]
+    b = W.random_batch(81, batch=len(lens), page_size=16, num_q_heads=32, num_kv_heads=8,
+                       head_dim=128, kv_dtype="bf16", q_dtype="bf16", min_len=0, max_len=0,
+                       partition_tokens=128, lens=lens, share=[([2, 3, 6], 20)])
+    pool, csr, q = to_device(b)
+    ro, rl = oatt.decode_attention(b)
+    for enabled in (0, 1):
+        plan = gpu.CascadePlan(b.indptr, b.indices, b.kv_len, 16,
+                               gpu.CascadeParams(enabled=enabled, min_shared_pages=4,
+                                                 l0_partition_tokens=64, l1_partition_tokens=128))
+        outs = []
+        for _ in range(3):
+            o, l = plan.run(pool, q, b.sm_scale)
+            torch.cuda.synchronize()
+            outs.append((o.cpu().numpy(), l.cpu().numpy()))
+        assert plan.stats()[0]["members"] == (3 if enabled else 0)
+        for o, l in outs[1:]:
+            assert np.array_equal(o, outs[0][0]) and np.array_equal(l, outs[0][1])
+        o, l = outs[0]
+        assert_close(o, ro, TOL["bf16"], "planned out")
+        assert_lse(l, rl, "planned lse")
+        assert np.all(o[[1, 5]] == 0) and np.all(l[[1, 5]] == -np.inf)
