@@ -149,12 +149,17 @@ int merge_rows(const float* v_in, const float* lse_in, int num_in, const int* o_
                       stream);
 }
 
-// Kernel choice for one partial launch: the vector path owns up to 16 query
-// rows per KV head in registers; more rows are tiled over several
-// workgroups (each tile re-reads the KV range, mostly from L2).
+// Kernel choice for one partial launch: the matrix-core path when a KV head
+// serves at least 16 bf16 query rows (stacked level 0, MLA); otherwise the
+// vector path, which keeps up to 16 query rows per KV head in registers and
+// tiles more rows over several workgroups.
 int launch_partial(const PartialArgs& a, hipStream_t stream) {
+  bool handled = false;
+  int st = launch_partial_mfma(a, stream, &handled);
+  if (st || handled) return st;
   if (a.kv_dtype == PDK_FP8_E4M3)
-    return fail(PDK_ERR_UNSUPPORTED, "fp8 pools need the matrix-core path");
+    return fail(PDK_ERR_UNSUPPORTED, "fp8 pools are read by the matrix-core path only "
+                                     "(bf16 queries, >= 64 query rows, head dims 576/512)");
   return launch_partial_valu(a, stream);
 }
 

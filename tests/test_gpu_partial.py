@@ -71,6 +71,9 @@ def test_lengths_around_boundaries(gpu, page_size, S):
     (8, 2, 256, "bf16", "bf16"),     # D = 256
     (8, 2, 128, "bf16", "f32"),      # f32 queries on a bf16 pool
     (8, 2, 64, "f32", "bf16"),       # bf16 queries on an f32 pool
+    (64, 2, 128, "bf16", "bf16"),    # G = 32: matrix-core tile of 32 rows
+    (48, 1, 128, "bf16", "bf16"),    # G = 48: 64-row tile, 16 rows padded
+    (160, 1, 128, "bf16", "bf16"),   # G = 160: three 64-row tiles
 ])
 def test_head_groupings_and_dtypes(gpu, Hq, Hkv, D, kv, qd):
     b = W.random_batch(60 + Hq + D, batch=5, page_size=16, num_q_heads=Hq, num_kv_heads=Hkv,
