@@ -51,40 +51,46 @@ def device_batch(torch, pdk, b, device):
 
 
 class Timer:
-    """HIP events on the current stream around each step of the timed loop.
-
-    Every launch of the path is enqueued on the current (torch) stream, so
-    the events bracket exactly the kernels of the step."""
+    """HIP events on the current stream: every launch of the path is
+    enqueued on the current (torch) stream, so an event pair brackets exactly
+    the launches issued between its two records."""
 
     def __init__(self, torch):
         self.torch = torch
-        self.pairs = []
+        self.marks = []
 
-    def run(self, fn):
-        s = self.torch.cuda.Event(enable_timing=True)
+    def mark(self):
         e = self.torch.cuda.Event(enable_timing=True)
-        s.record()
-        fn()
         e.record()
-        self.pairs.append((s, e))
+        self.marks.append(e)
+        return len(self.marks) - 1
 
-    def mean_us(self):
-        return 1000.0 * sum(s.elapsed_time(e) for s, e in self.pairs) / len(self.pairs)
+    def mean_us(self, pairs):
+        return 1000.0 * sum(self.marks[a].elapsed_time(self.marks[b]) for a, b in pairs) / len(pairs)
 
 
-def time_steps(torch, step, steps, warmup):
-    """Wall time per step over exactly `steps` steps (synchronized on both
-    sides), plus the event-measured device time of each step."""
+def time_steps(torch, parts, steps, warmup):
+    """Exactly `steps` steps, synchronized on both sides; each step runs the
+    callables in `parts` in order with an event between consecutive ones.
+    Returns the wall time per step (ms) and the mean device time of each
+    part (us), measured by the events."""
     for _ in range(warmup):
-        step()
+        for f in parts:
+            f()
     torch.cuda.synchronize()
     timer = Timer(torch)
+    spans = [[] for _ in parts]
     t0 = time.perf_counter()
     for _ in range(steps):
-        timer.run(step)
+        a = timer.mark()
+        for i, f in enumerate(parts):
+            f()
+            b = timer.mark()
+            spans[i].append((a, b))
+            a = b
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1000.0 / steps
-    return wall_ms, timer.mean_us()
+    return wall_ms, [timer.mean_us(sp) for sp in spans]
 
 
 def cpu_baseline(batches, budget_s=15.0):
@@ -119,10 +125,13 @@ def planned(torch, pdk, b, params, dev):
 
 
 def run_plan_steps(args, torch, pdk, b, pool, q, plan, dev):
+    """Timed steps of a planned decode: (wall ms per step, partials us, merge us)."""
     out = torch.empty((b.batch, b.num_q_heads, b.head_dim_v), dtype=torch.float32, device=dev)
     lse = torch.empty((b.batch, b.num_q_heads), dtype=torch.float32, device=dev)
-    return time_steps(torch, lambda: plan.run(pool, q, b.sm_scale, out, lse), args.steps,
-                      args.warmup)
+    wall_ms, (t_part, t_merge) = time_steps(
+        torch, [lambda: plan.run_partials(pool, q, b.sm_scale), lambda: plan.run_merge(out, lse)],
+        args.steps, args.warmup)
+    return wall_ms, t_part, t_merge
 
 
 def bench_flat(args, torch, pdk, W, dev):
@@ -130,17 +139,17 @@ def bench_flat(args, torch, pdk, W, dev):
     pool, csr, q = device_batch(torch, pdk, b, dev)
     S = b.partition_tokens
     plan, plan_us = planned(torch, pdk, b, pdk.CascadeParams(enabled=0, l1_partition_tokens=S), dev)
-    wall_ms, dev_us = run_plan_steps(args, torch, pdk, b, pool, q, plan, dev)
+    wall_ms, t_part, t_merge = run_plan_steps(args, torch, pdk, b, pool, q, plan, dev)
     stats, _ = plan.stats()
     R = stats["suffix_chunks"]
     Hq, Dv = b.num_q_heads, b.head_dim_v
     kv = b.unique_kv_bytes()
-    # the one kernel of the step: KV read once, q, partial states written and
-    # read back by the fused merge, merged output written, page table
-    alg = (kv + b.q.nbytes + 2 * R * Hq * (Dv + 1) * 4 + b.batch * Hq * (Dv + 1) * 4
-           + b.indices.nbytes + b.kv_len.nbytes)
+    # the dominant kernel (partials): every KV byte once, the queries, the
+    # page table, and the partial states it writes
+    alg = (kv + b.q.nbytes + R * Hq * (Dv + 1) * 4 + b.indices.nbytes + b.kv_len.nbytes
+           + (b.batch + 1) * 4)
     value = kv / (wall_ms * 1e-3) / 1e9
-    achieved = alg / (dev_us * 1e-6) / 1e9
+    achieved = alg / (t_part * 1e-6) / 1e9
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 5),
@@ -157,9 +166,11 @@ def bench_flat(args, torch, pdk, W, dev):
         "unique_kv_bytes": kv,
         "plan_host_us": round(plan_us, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "partial_valu_kernel<bf16,bf16,D128,4 rows> with fused merge",
-                     "kernel_us": round(dev_us, 2), "bytes_per_launch": alg},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_record("partial_valu.hip"),
+                     "kernel": "partial_valu_kernel<bf16,bf16,D128,4 rows>",
+                     "kernel_us": round(t_part, 2), "bytes_per_launch": alg},
+        "kernels_us": {"partials": round(t_part, 2), "merge": round(t_merge, 2)},
     }
     batches = [b]
     if not args.no_cascade:
@@ -167,6 +178,63 @@ def bench_flat(args, torch, pdk, W, dev):
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(batches)
     return res
+
+
+def traffic_record(kernel_source, launches_per_step=1):
+    """HBM bytes per launch from the committed rocprofv3 counter record,
+    or None when the kernel source has changed since it was taken."""
+    import hashlib
+    rec_path = os.path.join(ROOT, "profiles", "traffic.json")
+    src_path = os.path.join(ROOT, "paged_split_kv_v2_amd", "csrc", kernel_source)
+    if not (os.path.exists(rec_path) and os.path.exists(src_path)):
+        return None
+    rec = json.load(open(rec_path)).get(kernel_source)
+    sha = hashlib.sha256(open(src_path, "rb").read()).hexdigest()
+    if not rec or rec.get("source_sha256") != sha:
+        return None
+    return int(rec["fetch_kib_per_dispatch"] * 1024 * rec["fetch_factor"] +
+               rec["write_kib_per_dispatch"] * 1024 * rec["write_factor"])
+
+
+def bench_merge(args, torch, pdk, W, dev):
+    """merge_states on 8192 output rows, H 32, D 128, 1..16 rows per group."""
+    m = W.merge_microbench()
+    v = torch.from_numpy(m.v_in).to(dev)
+    l = torch.from_numpy(m.lse_in).to(dev)
+    ind = torch.from_numpy(m.o_indptr).to(dev)
+    M = len(m.o_indptr) - 1
+    vo = torch.empty((M, v.shape[1], v.shape[2]), dtype=torch.float32, device=dev)
+    lo = torch.empty((M, v.shape[1]), dtype=torch.float32, device=dev)
+    wall_ms, (dev_us,) = time_steps(torch, [lambda: pdk.merge_states(v, l, ind, vo, lo)],
+                                    args.steps, args.warmup)
+    alg = m.v_in.nbytes + m.lse_in.nbytes + m.o_indptr.nbytes + vo.numel() * 4 + lo.numel() * 4
+    value = alg / (wall_ms * 1e-3) / 1e9
+    achieved = alg / (dev_us * 1e-6) / 1e9
+    return {"metric": "merge_states HBM GB/s", "value": round(value, 2), "unit": "GB/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(wall_ms, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "merge_states_m8192_h32_d128", "out_rows": M,
+                       "in_rows": int(m.o_indptr[-1]), "heads": 32, "head_dim": 128},
+            "us_per_step": round(wall_ms * 1000, 2),
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "traffic": traffic_record("merge.hip"), "kernel": "merge_kernel",
+                         "kernel_us": round(dev_us, 2), "bytes_per_launch": alg}}
+
+
+def bench_copy(args, torch, pdk, W, dev):
+    """Calibration: a plain device copy of 1 GiB (torch's copy kernel), the
+    reference for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    n = 1 << 30
+    x = torch.empty(n // 2, dtype=torch.bfloat16, device=dev).normal_()
+    y = torch.empty_like(x)
+    wall_ms, (dev_us,) = time_steps(torch, [lambda: y.copy_(x)], args.steps, args.warmup)
+    return {"metric": "device copy GB/s (read + write)", "value": round(2 * n / (dev_us * 1e-6) / 1e9, 2),
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(wall_ms, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "copy_1GiB", "bytes_read": n, "bytes_written": n}}
 
 
 def bench_cascade_arms(args, torch, pdk, W, dev):
@@ -186,9 +254,10 @@ def bench_cascade_arms(args, torch, pdk, W, dev):
                                                      l0_partition_tokens=256,
                                                      l1_partition_tokens=512))):
         plan, plan_us = planned(torch, pdk, b, params, dev)
-        wall_ms, dev_us = run_plan_steps(args, torch, pdk, b, pool, q, plan, dev)
+        wall_ms, t_part, t_merge = run_plan_steps(args, torch, pdk, b, pool, q, plan, dev)
         stats, decline = plan.stats()
-        arms[name] = {"us_per_step": round(wall_ms * 1000, 2), "device_us": round(dev_us, 2),
+        arms[name] = {"us_per_step": round(wall_ms * 1000, 2),
+                      "partials_us": round(t_part, 2), "merge_us": round(t_merge, 2),
                       "unique_kv_GBps": round(kv / (wall_ms * 1e-3) / 1e9, 2),
                       "frac_of_peak": round(kv / (wall_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                       "plan_host_us": round(plan_us, 1), "members": stats["members"],
@@ -207,7 +276,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="flat", choices=["flat"])
+    ap.add_argument("--workload", default="flat", choices=["flat", "merge", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cascade", action="store_true")
     args = ap.parse_args()
@@ -222,7 +291,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     pdk.lib()
-    res = {"flat": bench_flat}[args.workload](args, torch, pdk, W, "cuda:0")
+    res = {"flat": bench_flat, "merge": bench_merge,
+           "copy": bench_copy}[args.workload](args, torch, pdk, W, "cuda:0")
     print(json.dumps(res), flush=True)
 
 

@@ -274,6 +274,17 @@ int pdk_run_cascade_decode(const pdk_cascade_plan* plan, const pdk_kv_pool* pool
                            float* lse_out, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
+/* The two halves of pdk_run_cascade_decode, for callers that enqueue other
+ * work (or timing events) between them: the level-0 and level-1 partial
+ * launches into the workspace, then the single merge into out / lse_out.
+ * Same arguments and errors; the merge needs the head dim of the values. */
+int pdk_run_cascade_partials(const pdk_cascade_plan* plan, const pdk_kv_pool* pool,
+                             const void* q, int32_t q_dtype, int32_t num_q_heads, float sm_scale,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+int pdk_run_cascade_merge(const pdk_cascade_plan* plan, int32_t num_q_heads, int32_t head_dim_v,
+                          float* out, float* lse_out, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
 /* ---------------------------------------------------------------------- */
 /* Chunked cached prefix + new suffix (one GPU's share of MLA decode)      */
 /* [DCP-PR, 3.2 figure]                                                    */

@@ -90,6 +90,8 @@ _SIGS = {
     "pdk_cascade_workspace_bytes": (_S, [_P, _I, _I]),
     "pdk_cascade_plan_upload": (_I, [_P, _P, _S, _P]),
     "pdk_run_cascade_decode": (_I, [_P, _P, _P, _I, _I, _F, _P, _P, _P, _S, _P]),
+    "pdk_run_cascade_partials": (_I, [_P, _P, _P, _I, _I, _F, _P, _S, _P]),
+    "pdk_run_cascade_merge": (_I, [_P, _I, _I, _P, _P, _P, _S, _P]),
     "pdk_chunked_plan_create": (_I, [_P, _I, _I, _I, _P, _I, _I, _P]),
     "pdk_chunked_plan_free": (None, [_P]),
     "pdk_chunked_plan_counts": (_I, [_P, _P]),
@@ -407,6 +409,24 @@ class CascadePlan:
                                             Hq, float(sm_scale), _ptr(out), _ptr(lse_out),
                                             _ptr(self.workspace), int(self.workspace.numel()),
                                             _stream(stream)))
+        return out, lse_out
+
+    def run_partials(self, pool: KVPool, q: torch.Tensor, sm_scale: float, stream=None):
+        """Level-0 and level-1 partial launches only (into the workspace)."""
+        Hq = int(q.shape[1])
+        if self.workspace is None:
+            self.upload(Hq, pool.head_dim_v, q.device, stream)
+        ps = pool.struct()
+        _check(lib().pdk_run_cascade_partials(self._h, ctypes.byref(ps), _ptr(q), _dtype_code(q),
+                                              Hq, float(sm_scale), _ptr(self.workspace),
+                                              int(self.workspace.numel()), _stream(stream)))
+
+    def run_merge(self, out: torch.Tensor, lse_out: Optional[torch.Tensor], stream=None):
+        """The single merge of the workspace's partial rows into out / lse_out."""
+        Hq, Dv = int(out.shape[1]), int(out.shape[2])
+        _check(lib().pdk_run_cascade_merge(self._h, Hq, Dv, _ptr(out), _ptr(lse_out),
+                                           _ptr(self.workspace), int(self.workspace.numel()),
+                                           _stream(stream)))
         return out, lse_out
 
 

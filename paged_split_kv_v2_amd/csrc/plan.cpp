@@ -342,10 +342,10 @@ int pdk_cascade_plan_upload(pdk_cascade_plan* plan, void* ws, size_t ws_bytes, h
   return PDK_OK;
 }
 
-int pdk_run_cascade_decode(const pdk_cascade_plan* plan, const pdk_kv_pool* pool, const void* q,
-                           int32_t q_dtype, int32_t Hq, float sm_scale, float* out,
-                           float* lse_out, void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (!plan || !pool || !q || !out || !ws) return fail(PDK_ERR_ARG, "NULL argument");
+int pdk_run_cascade_partials(const pdk_cascade_plan* plan, const pdk_kv_pool* pool,
+                             const void* q, int32_t q_dtype, int32_t Hq, float sm_scale,
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!plan || !pool || !q || !ws) return fail(PDK_ERR_ARG, "NULL argument");
   if (pool->page_size != plan->page_size)
     return fail(PDK_ERR_SHAPE, "pool page size %d != plan page size %d", pool->page_size,
                 plan->page_size);
@@ -372,14 +372,35 @@ int pdk_run_cascade_decode(const pdk_cascade_plan* plan, const pdk_kv_pool* pool
   }
   // level 1: every request's remaining range (the flat batch when declined)
   pdk_csr v1{base + o.l1_indptr, base + o.l1_indices, base + o.l1_len, plan->batch, 0};
-  int st = partial_rows(pool, &v1, q, q_dtype, Hq, sm_scale, plan->params.l1_partition_tokens,
-                        base + o.l1_parts, plan->n_l1_parts, nullptr, nullptr, 0, G,
-                        base + o.l1_rows, v_part, lse_part, stream,
-                        reinterpret_cast<const int2*>(base + o.l1_work));
-  if (st) return st;
+  return partial_rows(pool, &v1, q, q_dtype, Hq, sm_scale, plan->params.l1_partition_tokens,
+                      base + o.l1_parts, plan->n_l1_parts, nullptr, nullptr, 0, G,
+                      base + o.l1_rows, v_part, lse_part, stream,
+                      reinterpret_cast<const int2*>(base + o.l1_work));
+}
+
+int pdk_run_cascade_merge(const pdk_cascade_plan* plan, int32_t Hq, int32_t Dv, float* out,
+                          float* lse_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!plan || !out || !ws) return fail(PDK_ERR_ARG, "NULL argument");
+  if (plan->uploaded_to != ws)
+    return fail(PDK_ERR_WORKSPACE, "plan was not uploaded to this workspace");
+  const size_t need = pdk_cascade_workspace_bytes(plan, Hq, Dv);
+  if (need == 0 || ws_bytes < need)
+    return fail(PDK_ERR_WORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
+  const int32_t* base = (const int32_t*)ws;
+  float* v_part = (float*)((char*)ws + cascade_state_offset(plan));
+  float* lse_part = (float*)((char*)v_part + align256((size_t)plan->total_rows * Hq * Dv * 4));
   // one merge per request over its [level-0][level-1] rows
-  return pdk_merge_states(v_part, lse_part, plan->total_rows, base + o.fused, plan->batch, Hq,
-                          pool->head_dim_v, out, lse_out, stream);
+  return pdk_merge_states(v_part, lse_part, plan->total_rows, base + plan->off.fused, plan->batch,
+                          Hq, Dv, out, lse_out, stream);
+}
+
+int pdk_run_cascade_decode(const pdk_cascade_plan* plan, const pdk_kv_pool* pool, const void* q,
+                           int32_t q_dtype, int32_t Hq, float sm_scale, float* out,
+                           float* lse_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!out) return fail(PDK_ERR_ARG, "NULL out");
+  int st = pdk_run_cascade_partials(plan, pool, q, q_dtype, Hq, sm_scale, ws, ws_bytes, stream);
+  if (st) return st;
+  return pdk_run_cascade_merge(plan, Hq, pool->head_dim_v, out, lse_out, ws, ws_bytes, stream);
 }
 
 // ---------------------------------------------------------------------------
