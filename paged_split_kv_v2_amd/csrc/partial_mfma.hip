@@ -14,10 +14,13 @@
 //
 // Workgroup = NW waves, wave w owns query rows [16w, 16w+16) of the row tile.
 // Per tile of TT tokens:
-//   * global -> registers (next tile, issued before the current one is
-//     computed) -> LDS: K row-major [token][dim] (bf16, fp8 rows dequantized
-//     on the way: RNE_bf16(f32(x) * scale)); V transposed [dim][token],
-//     written as packed token pairs;
+//   * global -> registers -> LDS, double-buffered: the next tile's loads are
+//     issued in two halves, stored to the other LDS buffer after the QK
+//     products and after the PV products respectively, so at most half a
+//     tile of raw rows is held in registers and one barrier per tile
+//     suffices. K is stored row-major [token][dim] (bf16; fp8 rows are
+//     dequantized on the way: RNE_bf16(f32(x) * scale)); V transposed
+//     [dim][token], written as packed token pairs;
 //   * S^T = K . Q^T with v_mfma_f32_16x16x32_bf16: A = 16 K rows from LDS,
 //     B = the wave's 16 query rows (registers, loaded once). Each lane's
 //     accumulator then holds one query row for four tokens;
@@ -71,20 +74,21 @@ __global__ __launch_bounds__(64 * NW) void partial_mfma_kernel(const PartialArgs
   constexpr int DB = DV / 16;                    // 16-wide output column blocks
   constexpr int KLD = DK + 8;                    // LDS row of K (bf16), padded 16 B
   constexpr int VLD = TT + 4;                    // LDS row of V^T (bf16), padded 8 B
-  constexpr int KCW = (KT == MK_FP8) ? 16 : 8;   // K elements per 16-byte chunk
+  constexpr int KCW = (KT == MK_FP8) ? 16 : 8;   // elements per 16-byte chunk
   constexpr int KCH = DK / KCW;                  // chunks per K row
-  constexpr int KPAIRS = (TT / 2) * KCH;         // (token pair, chunk) items per tile
-  constexpr int KIT = (KPAIRS + NT - 1) / NT;
-  constexpr int VCW = (KT == MK_FP8) ? 16 : 8;
-  constexpr int VCH = DV / VCW;
+  constexpr int VCH = DV / KCW;                  // chunks per V row
+  constexpr int KPAIRS = (TT / 2) * KCH;         // (token pair, chunk) items of K per tile
   constexpr int VPAIRS = LATENT ? 0 : (TT / 2) * VCH;
-  constexpr int VIT = LATENT ? 0 : (VPAIRS + NT - 1) / NT;
+  constexpr int ITEMS = KPAIRS + VPAIRS;
+  constexpr int NIT = (ITEMS + NT - 1) / NT;     // items per thread per tile
+  constexpr int NA = (NIT + 1) / 2;              // first half: staged after the QK products
   constexpr int KW = KCW / 2;                    // bf16 words of a converted chunk
   static_assert(DK % 32 == 0 && DV % 16 == 0 && TT % 32 == 0, "tile shapes");
   static_assert(!LATENT || (DV <= DK && DV % KCW == 0), "latent value lanes");
 
-  __shared__ __align__(16) uint16_t sm_k[TT * KLD];
-  __shared__ __align__(16) uint16_t sm_vt[DV * VLD];
+  // two LDS buffers: the next tile is staged while the current one is read
+  __shared__ __align__(16) uint16_t sm_k[2][TT * KLD];
+  __shared__ __align__(16) uint16_t sm_vt[2][DV * VLD];
   __shared__ int sm_pid[kMaxPartPagesM];
 
   const int n_tiles = (a.max_rows + 16 * NW - 1) / (16 * NW);
@@ -163,35 +167,35 @@ __global__ __launch_bounds__(64 * NW) void partial_mfma_kernel(const PartialArgs
   const long long vb_stride = (LATENT ? a.k_bstride : a.v_bstride) * ESZ;
   const int krow = DK * ESZ, vrow = (LATENT ? DK : DV) * ESZ;
 
-  u32x4_t kr[KIT][2];
-  u32x4_t vr[VIT > 0 ? VIT : 1][2];
+  u32x4_t raw[NIT][2];  // staged items: two tokens of one 16-byte chunk each
 
   auto row_addr = [&](const char* base, long long bstride, int rowb, int t) {
     const int tc = min(t, end - 1);
     const int pid = sm_pid[(tc >> shift) - pg_first];
     return base + pid * bstride + (tc & pmask) * rowb;
   };
+  // item c < KPAIRS: K chunk (token pair c / KCH, chunk c % KCH); else V
+  auto is_k = [&](int it, int c) {
+    if constexpr (KPAIRS % NT == 0) return it < KPAIRS / NT;
+    else return c < KPAIRS;
+  };
 
-  auto load_tile = [&](int t0) {
+  auto load_items = [&](int it0, int it1, int t0) {
 #pragma unroll
-    for (int it = 0; it < KIT; ++it) {
+    for (int it = it0; it < it1; ++it) {
       const int c = tid + it * NT;
-      if (KPAIRS % NT == 0 || c < KPAIRS) {
-        const int tp = c / KCH, cc = c - (c / KCH) * KCH;
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-          kr[it][s] = ld_nt16(row_addr(kbase, kb_stride, krow, t0 + 2 * tp + s) + cc * 16);
-      }
-    }
-    if constexpr (!LATENT) {
-#pragma unroll
-      for (int it = 0; it < VIT; ++it) {
-        const int c = tid + it * NT;
-        if (VPAIRS % NT == 0 || c < VPAIRS) {
-          const int tp = c / VCH, vc = c - (c / VCH) * VCH;
+      if (ITEMS % NT == 0 || c < ITEMS) {
+        if (is_k(it, c)) {
+          const int tp = c / KCH, cc = c - tp * KCH;
 #pragma unroll
           for (int s = 0; s < 2; ++s)
-            vr[it][s] = ld_nt16(row_addr(vbase, vb_stride, vrow, t0 + 2 * tp + s) + vc * 16);
+            raw[it][s] = ld_nt16(row_addr(kbase, kb_stride, krow, t0 + 2 * tp + s) + cc * 16);
+        } else {
+          const int c2 = c - KPAIRS;
+          const int tp = c2 / VCH, vc = c2 - tp * VCH;
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+            raw[it][s] = ld_nt16(row_addr(vbase, vb_stride, vrow, t0 + 2 * tp + s) + vc * 16);
         }
       }
     }
@@ -208,43 +212,58 @@ __global__ __launch_bounds__(64 * NW) void partial_mfma_kernel(const PartialArgs
     }
   };
 
-  auto store_tile = [&]() {
+  auto store_items = [&](int it0, int it1, int bf) {
 #pragma unroll
-    for (int it = 0; it < KIT; ++it) {
+    for (int it = it0; it < it1; ++it) {
       const int c = tid + it * NT;
-      if (KPAIRS % NT == 0 || c < KPAIRS) {
-        const int tp = c / KCH, cc = c - (c / KCH) * KCH;
-        uint32_t w[2][KW];
-        convert(kr[it][0], w[0], a.k_scale);
-        convert(kr[it][1], w[1], a.k_scale);
+      if (ITEMS % NT == 0 || c < ITEMS) {
+        if (is_k(it, c)) {
+          const int tp = c / KCH, cc = c - tp * KCH;
+          const bool vt = LATENT && cc * KCW < DV;  // these lanes are also values
+          if constexpr (KT == MK_FP8) {
+            // four codes of each token at a time: 8-byte K pieces, 4 V^T pairs
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
+            for (int i = 0; i < 4; ++i) {
+              uint32_t w0[2], w1[2];
+              fp8x4_dequant_bf16(raw[it][0][i], a.k_scale, w0[0], w0[1]);
+              fp8x4_dequant_bf16(raw[it][1][i], a.k_scale, w1[0], w1[1]);
+              *reinterpret_cast<u32x2_t*>(&sm_k[bf][(2 * tp) * KLD + cc * KCW + 4 * i]) =
+                  u32x2_t{w0[0], w0[1]};
+              *reinterpret_cast<u32x2_t*>(&sm_k[bf][(2 * tp + 1) * KLD + cc * KCW + 4 * i]) =
+                  u32x2_t{w1[0], w1[1]};
+              if (vt) {
 #pragma unroll
-          for (int i = 0; i < KW / 4; ++i)
-            *reinterpret_cast<u32x4_t*>(&sm_k[(2 * tp + s) * KLD + cc * KCW + 8 * i]) =
-                u32x4_t{w[s][4 * i], w[s][4 * i + 1], w[s][4 * i + 2], w[s][4 * i + 3]};
-        if constexpr (LATENT) {
-          if (cc * KCW < DV) {
+                for (int e = 0; e < 4; ++e)
+                  *reinterpret_cast<uint32_t*>(&sm_vt[bf][(cc * KCW + 4 * i + e) * VLD + 2 * tp]) =
+                      pair_word(w0, w1, e);
+              }
+            }
+          } else {
+            uint32_t w[2][KW];
+            convert(raw[it][0], w[0], a.k_scale);
+            convert(raw[it][1], w[1], a.k_scale);
 #pragma unroll
-            for (int e = 0; e < KCW; ++e)
-              *reinterpret_cast<uint32_t*>(&sm_vt[(cc * KCW + e) * VLD + 2 * tp]) =
-                  pair_word(w[0], w[1], e);
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+              for (int i = 0; i < KW / 4; ++i)
+                *reinterpret_cast<u32x4_t*>(&sm_k[bf][(2 * tp + s) * KLD + cc * KCW + 8 * i]) =
+                    u32x4_t{w[s][4 * i], w[s][4 * i + 1], w[s][4 * i + 2], w[s][4 * i + 3]};
+            if (vt) {
+#pragma unroll
+              for (int e = 0; e < KCW; ++e)
+                *reinterpret_cast<uint32_t*>(&sm_vt[bf][(cc * KCW + e) * VLD + 2 * tp]) =
+                    pair_word(w[0], w[1], e);
+            }
           }
-        }
-      }
-    }
-    if constexpr (!LATENT) {
+        } else {
+          uint32_t w[2][KW];
+          const int c2 = c - KPAIRS;
+          const int tp = c2 / VCH, vc = c2 - tp * VCH;
+          convert(raw[it][0], w[0], a.v_scale);
+          convert(raw[it][1], w[1], a.v_scale);
 #pragma unroll
-      for (int it = 0; it < VIT; ++it) {
-        const int c = tid + it * NT;
-        if (VPAIRS % NT == 0 || c < VPAIRS) {
-          const int tp = c / VCH, vc = c - (c / VCH) * VCH;
-          uint32_t w[2][VCW / 2];
-          convert(vr[it][0], w[0], a.v_scale);
-          convert(vr[it][1], w[1], a.v_scale);
-#pragma unroll
-          for (int e = 0; e < VCW; ++e)
-            *reinterpret_cast<uint32_t*>(&sm_vt[(vc * VCW + e) * VLD + 2 * tp]) =
+          for (int e = 0; e < KCW; ++e)
+            *reinterpret_cast<uint32_t*>(&sm_vt[bf][(vc * KCW + e) * VLD + 2 * tp]) =
                 pair_word(w[0], w[1], e);
         }
       }
@@ -257,12 +276,15 @@ __global__ __launch_bounds__(64 * NW) void partial_mfma_kernel(const PartialArgs
   float run_m = -INFINITY, run_l = 0.f;
 
   __syncthreads();  // page ids visible
-  if (start < end) load_tile(start);
+  if (start < end) {
+    load_items(0, NIT, start);
+    store_items(0, NIT, 0);
+  }
+  __syncthreads();
+  int bf = 0;
   for (int t0 = start; t0 < end; t0 += TT) {
-    __syncthreads();  // previous tile's LDS reads are done
-    store_tile();
-    __syncthreads();
-    if (t0 + TT < end) load_tile(t0 + TT);
+    const bool more = t0 + TT < end;  // uniform
+    if (more) load_items(0, NA, t0 + TT);
 
     // S^T = K . Q^T for the wave's 16 query rows
     f32x4_t s[TB];
@@ -271,12 +293,17 @@ __global__ __launch_bounds__(64 * NW) void partial_mfma_kernel(const PartialArgs
       s[tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
-        const u32x4_t kf =
-            *reinterpret_cast<const u32x4_t*>(&sm_k[(16 * tb + r16) * KLD + 32 * ks + 8 * q4]);
+        const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(
+            &sm_k[bf][(16 * tb + r16) * KLD + 32 * ks + 8 * q4]);
         s[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(qf[ks]), s[tb],
                                                         0, 0, 0);
       }
     }
+    if (more) {
+      store_items(0, NA, bf ^ 1);
+      load_items(NA, NIT, t0 + TT);
+    }
+
     // scale, mask tokens past the end, row max across the four lane groups
     float mx = -INFINITY;
 #pragma unroll
@@ -327,7 +354,7 @@ __global__ __launch_bounds__(64 * NW) void partial_mfma_kernel(const PartialArgs
       if constexpr (SPLIT) pl = as_bf16x8(u32x4_t{lw[0], lw[1], lw[2], lw[3]});
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const uint16_t* vp = &sm_vt[(16 * db + r16) * VLD + 32 * kb + 4 * q4];
+        const uint16_t* vp = &sm_vt[bf][(16 * db + r16) * VLD + 32 * kb + 4 * q4];
         const u32x2_t v0 = *reinterpret_cast<const u32x2_t*>(vp);
         const u32x2_t v1 = *reinterpret_cast<const u32x2_t*>(vp + 16);
         const bf16x8_t vf = as_bf16x8(u32x4_t{v0[0], v0[1], v1[0], v1[1]});
@@ -336,6 +363,9 @@ __global__ __launch_bounds__(64 * NW) void partial_mfma_kernel(const PartialArgs
           acc_o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl, acc_o[db], 0, 0, 0);
       }
     }
+    if (more) store_items(NA, NIT, bf ^ 1);
+    __syncthreads();  // next tile staged; this tile's buffer free again
+    bf ^= 1;
   }
 
   // row sum across the lane groups, then the normalized partial and its LSE
@@ -346,16 +376,13 @@ __global__ __launch_bounds__(64 * NW) void partial_mfma_kernel(const PartialArgs
     const int m = my_row / a.G, g = my_row % a.G;
     const int orow = (stacked ? a.out_row_base[mbase + m] : a.out_row_base[b]) + p;
     const size_t o = (size_t)orow * a.Hq + h * a.G + g;
-    const float inv = (l > 0.f) ? 1.f / l : 0.f;
     float* dst = a.v_out + o * DV + 4 * q4;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      float4 x;
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
       if (l > 0.f) x = make_float4(acc_o[db][0] / l, acc_o[db][1] / l, acc_o[db][2] / l, acc_o[db][3] / l);
-      else x = make_float4(0.f, 0.f, 0.f, 0.f);
       *reinterpret_cast<float4*>(dst + 16 * db) = x;
     }
-    (void)inv;
     if (q4 == 0) a.lse_out[o] = (l > 0.f) ? run_m + log2f(l) : -INFINITY;
   }
 }

@@ -1,0 +1,64 @@
+"""Chunked cached-prefix + new-suffix decode of an MLA share on the GPU
+[DCP-PR, section 3.2 figure: each cached-prefix chunk returns (O, LSE); the
+chunk states are LSE-merged, then merged with the new-token suffix state;
+3.3: fp8 rows are dequantized to bf16 with the per-tensor scale].
+
+Checked against the oracle's chunk states and against the plain definition
+(one softmax over prefix and suffix tokens), tolerance 5e-3 (fp8 KV after the
+identical dequant), LSE within 1e-4."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import mla as omla
+from gpu_util import TOL, assert_close, assert_lse, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def run_chunked(pdk, share):
+    pre, suf = share.prefix, share.suffix
+    p_pool, _, q = to_device(pre)
+    s_pool, _, _ = to_device(suf)
+    plan = pdk.ChunkedPlan((pre.indptr, pre.indices, pre.kv_len), pre.page_size,
+                           share.chunk_tokens, pre.partition_tokens,
+                           (suf.indptr, suf.indices, suf.kv_len), suf.page_size,
+                           suf.partition_tokens)
+    counts = plan.counts()
+    Hq, Dv = pre.num_q_heads, pre.head_dim_v
+    chunk_out = torch.empty((counts["chunks"], Hq, Dv), dtype=torch.float32, device="cuda")
+    chunk_lse = torch.empty((counts["chunks"], Hq), dtype=torch.float32, device="cuda")
+    out, lse = plan.run(p_pool, s_pool, q, pre.sm_scale, chunk_out=chunk_out,
+                        chunk_lse=chunk_lse)
+    torch.cuda.synchronize()
+    return (out.cpu().numpy(), lse.cpu().numpy(), chunk_out.cpu().numpy(),
+            chunk_lse.cpu().numpy(), counts)
+
+
+@pytest.mark.parametrize("context,chunk,part", [(2048, 1024, 512), (1000, 512, 256)])
+def test_mla_share_small(gpu, context, chunk, part):
+    share = W.mla_decode_share(seed=3005, batch=3, heads=128, context=context,
+                               suffix_tokens=100, chunk_tokens=chunk, partition_tokens=part)
+    out, lse, cout, clse, counts = run_chunked(gpu, share)
+    assert counts["chunks"] == 3 * -(-context // chunk)
+    ro, rl, rco, rcl = omla.mla_decode(share)
+    assert_close(cout, rco, TOL["fp8_e4m3"], "chunk out")
+    assert_lse(clse, rcl, "chunk lse")
+    assert_close(out, ro, TOL["fp8_e4m3"], "out")
+    assert_lse(lse, rl, "lse")
+    fo, fl = omla.mla_flat(share)
+    assert_close(out, fo, TOL["fp8_e4m3"], "out vs one softmax")
+
+
+def test_mla_share_full_size_sampled(gpu):
+    """Batch 32, 128 heads, 16384 cached fp8 tokens in 4096-token chunks plus
+    256 bf16 suffix tokens: sampled requests against the definition."""
+    share = W.mla_decode_share()
+    out, lse, _, _, counts = run_chunked(gpu, share)
+    assert counts["chunks"] == 32 * 4
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    reqs = [0, 13, 31]
+    fo, fl = omla.mla_flat(share, requests=reqs)
+    assert_close(out[reqs], fo[reqs], TOL["fp8_e4m3"], "out")
+    assert_lse(lse[reqs], fl[reqs], "lse")

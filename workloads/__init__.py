@@ -320,7 +320,7 @@ def mla_decode_share(seed: int = 1005, batch: int = 32, heads: int = 128,
     of page 64; bf16 queries; scale 1/sqrt(576)."""
     rng = np.random.default_rng(seed)
     Dk, Dv = 576, 512
-    npg = context // page_size
+    npg = _pages(context, page_size)
     lists = [list(range(b * npg, (b + 1) * npg)) for b in range(batch)]
     prefix = paged_batch_from_lists("mla_prefix_fp8", rng, lists, [context] * batch,
                                     page_size=page_size, num_q_heads=heads, num_kv_heads=1,
@@ -332,7 +332,7 @@ def mla_decode_share(seed: int = 1005, batch: int = 32, heads: int = 128,
     suffix = paged_batch_from_lists("mla_suffix_bf16", rng, slists, [suffix_tokens] * batch,
                                     page_size=page_size, num_q_heads=heads, num_kv_heads=1,
                                     head_dim_k=Dk, head_dim_v=Dv, kv_dtype="bf16",
-                                    q_dtype="bf16", partition_tokens=max(suffix_tokens, page_size),
+                                    q_dtype="bf16", partition_tokens=spg * page_size,
                                     pad_blocks=4, latent=True, poison=poison)
     suffix.q = prefix.q  # one query token per sequence, shared by both ranges
     return MlaShare(prefix=prefix, suffix=suffix, chunk_tokens=chunk_tokens)
