@@ -223,6 +223,82 @@ def bench_merge(args, torch, pdk, W, dev):
                          "kernel_us": round(dev_us, 2), "bytes_per_launch": alg}}
 
 
+def bench_mla(args, torch, pdk, W, dev):
+    """One GPU's share of an MLA decode: 32 requests, 128 query heads, latent
+    576 (values = first 512 lanes), 16384 cached fp8 tokens in 4096-token
+    chunks (1024-token partitions) plus 256 new bf16 tokens. A step is the
+    whole pipeline: chunk partials, per-chunk merge, merge across chunks,
+    suffix partials and merge, final merge."""
+    share = W.mla_decode_share()
+    pre, suf = share.prefix, share.suffix
+    p_pool, p_csr, q = device_batch(torch, pdk, pre, dev)
+    s_pool, _, _ = device_batch(torch, pdk, suf, dev)
+    plan = pdk.ChunkedPlan((pre.indptr, pre.indices, pre.kv_len), pre.page_size,
+                           share.chunk_tokens, pre.partition_tokens,
+                           (suf.indptr, suf.indices, suf.kv_len), suf.page_size,
+                           suf.partition_tokens)
+    Hq, Dv = pre.num_q_heads, pre.head_dim_v
+    plan.upload(Hq, Dv, dev)
+    out = torch.empty((pre.batch, Hq, Dv), dtype=torch.float32, device=dev)
+    lse = torch.empty((pre.batch, Hq), dtype=torch.float32, device=dev)
+    wall_ms, (step_us,) = time_steps(
+        torch, [lambda: plan.run(p_pool, s_pool, q, pre.sm_scale, out, lse)], args.steps,
+        args.warmup)
+    # the dominant kernel on its own: the same partitions of the cached range
+    S = pre.partition_tokens
+    pind = pdk.partition_indptr(pre.kv_len, S)
+    pind_d = torch.from_numpy(pind).to(dev)
+    R = int(pind[-1])
+    vp = torch.empty((R, Hq, Dv), dtype=torch.float32, device=dev)
+    lp = torch.empty((R, Hq), dtype=torch.float32, device=dev)
+    _, (part_us,) = time_steps(
+        torch, [lambda: pdk.paged_decode_partial(p_pool, p_csr, q, pre.sm_scale, S, pind_d, R, vp,
+                                                 lp)], args.steps, args.warmup)
+    tok_pre = int(pre.kv_len.sum())
+    tok_suf = int(suf.kv_len.sum())
+    flop_tok = 2 * Hq * (pre.head_dim_k + Dv)
+    flops_step = flop_tok * (tok_pre + tok_suf)
+    flops_part = flop_tok * tok_pre
+    kv_bytes = pre.unique_kv_bytes() + suf.unique_kv_bytes()
+    return {"metric": "MLA decode share: MFMA TFLOP/s (frac of bf16 peak) + µs/step",
+            "value": round(flops_step / (wall_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(wall_ms, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16 (fp8 e4m3 KV dequantized to bf16)",
+            "data": "synthetic",
+            "config": {"workload": "mla_decode_share_b32_ctx16384_fp8", "batch": pre.batch,
+                       "num_q_heads": Hq, "head_dim_k": pre.head_dim_k, "head_dim_v": Dv,
+                       "page_size": pre.page_size, "chunk_tokens": share.chunk_tokens,
+                       "partition_tokens": S, "suffix_tokens": int(suf.kv_len[0])},
+            "us_per_step": round(wall_ms * 1000, 2), "step_device_us": round(step_us, 2),
+            "kv_bytes": kv_bytes,
+            "hbm_frac_of_peak": round(kv_bytes / (wall_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "roofline": {"bound": "mfma", "achieved": round(flops_part / (part_us * 1e-6) / 1e12, 2),
+                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(flops_part / (part_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "traffic": traffic_record("partial_mfma.hip"),
+                         "kernel": "partial_mfma_kernel<576,512,8 waves,32,fp8,latent>",
+                         "kernel_us": round(part_us, 2), "flops_per_launch": flops_part}}
+
+
+def bench_cascade(args, torch, pdk, W, dev):
+    """The shared-prefix workload alone: flat vs cascade arms; value = the
+    all-groups cascade's rate over unique KV bytes."""
+    cv = bench_cascade_arms(args, torch, pdk, W, dev)
+    best = cv["arms"]["cascade_all_groups"]
+    return {"metric": METRIC, "value": best["unique_kv_GBps"], "unit": "GB/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(best["us_per_step"] / 1000, 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "cascade_shared_prefix_b72", "batch": 72, "groups": 4,
+                       "members_per_group": 16, "prefix_tokens": 4096,
+                       "suffix_tokens": "uniform[64,1024]", "extra_requests": 8,
+                       "extra_tokens": 2048, "num_q_heads": 32, "num_kv_heads": 8,
+                       "head_dim": 128, "page_size": 16},
+            "us_per_step": best["us_per_step"], "frac_of_peak": best["frac_of_peak"],
+            "cascade_vs_flat": cv}
+
+
 def bench_copy(args, torch, pdk, W, dev):
     """Calibration: a plain device copy of 1 GiB (torch's copy kernel), the
     reference for scaling the FETCH_SIZE / WRITE_SIZE counters."""
@@ -276,7 +352,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="flat", choices=["flat", "merge", "copy"])
+    ap.add_argument("--workload", default="flat", choices=["flat", "cascade", "merge", "mla", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cascade", action="store_true")
     args = ap.parse_args()
@@ -291,7 +367,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     pdk.lib()
-    res = {"flat": bench_flat, "merge": bench_merge,
+    res = {"flat": bench_flat, "cascade": bench_cascade, "merge": bench_merge, "mla": bench_mla,
            "copy": bench_copy}[args.workload](args, torch, pdk, W, "cuda:0")
     print(json.dumps(res), flush=True)
 
