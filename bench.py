@@ -276,8 +276,8 @@ def bench_mla(args, torch, pdk, W, dev):
             "roofline": {"bound": "mfma", "achieved": round(flops_part / (part_us * 1e-6) / 1e12, 2),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(flops_part / (part_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                         "traffic": traffic_record("partial_mfma.hip"),
-                         "kernel": "partial_mfma_kernel<576,512,8 waves,32,fp8,latent>",
+                         "traffic": traffic_record("partial_latent.hip"),
+                         "kernel": "partial_latent_kernel<576,512,fp8>",
                          "kernel_us": round(part_us, 2), "flops_per_launch": flops_part}}
 
 

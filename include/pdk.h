@@ -308,11 +308,14 @@ size_t pdk_chunked_workspace_bytes(const pdk_chunked_plan* plan, int32_t num_q_h
 int pdk_chunked_plan_upload(pdk_chunked_plan* plan, void* workspace, size_t workspace_bytes,
                             hipStream_t stream);
 
-/* Chunk partials -> merge per chunk (chunk_out/chunk_lse, each chunk's
- * (O, LSE)) -> merge across each request's chunks -> suffix partials and
- * merge -> merge of the prefix state with the suffix state. chunk_out
- * [chunks, Hq, Dv] and chunk_lse [chunks, Hq] are caller buffers (may be NULL
- * to keep them inside the workspace). out [B, Hq, Dv], lse_out [B, Hq]. */
+/* With chunk_out/chunk_lse (caller buffers [chunks, Hq, Dv] and
+ * [chunks, Hq]): chunk partials -> merge per chunk (each chunk's (O, LSE),
+ * written there) -> merge across each request's chunks -> suffix partials
+ * and merge -> merge of the prefix state with the suffix state. With both
+ * NULL: chunk and suffix partials, then ONE merge over all partials of each
+ * request - the same merges regrouped (merging is associative, [cascade-PR,
+ * "How the #898 merge kernel is reused"]), equal up to f32 rounding.
+ * out [B, Hq, Dv], lse_out [B, Hq] (log2). */
 int pdk_run_chunked_decode(const pdk_chunked_plan* plan, const pdk_kv_pool* prefix_pool,
                            const pdk_kv_pool* suffix_pool, const void* q, int32_t q_dtype,
                            int32_t num_q_heads, float sm_scale, float* out, float* lse_out,

@@ -8,6 +8,7 @@
 namespace pdk {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bits_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t f32_bits(float f) { return __builtin_bit_cast(uint32_t, f); }
@@ -21,8 +22,9 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
   __bf16 h = static_cast<__bf16>(x);
   return (uint32_t)__builtin_bit_cast(uint16_t, h);
 }
+// Two at once (one v_cvt_pk_bf16_f32), lo in the low half.
 __device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi) {
-  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 // Four OCP E4M3FN codes (one per byte of `w`) -> binary32, exact

@@ -155,7 +155,9 @@ int merge_rows(const float* v_in, const float* lse_in, int num_in, const int* o_
 // tiles more rows over several workgroups.
 int launch_partial(const PartialArgs& a, hipStream_t stream) {
   bool handled = false;
-  int st = launch_partial_mfma(a, stream, &handled);
+  int st = launch_partial_latent(a, stream, &handled);
+  if (st || handled) return st;
+  st = launch_partial_mfma(a, stream, &handled);
   if (st || handled) return st;
   if (a.kv_dtype == PDK_FP8_E4M3)
     return fail(PDK_ERR_UNSUPPORTED, "fp8 pools are read by the matrix-core path only "

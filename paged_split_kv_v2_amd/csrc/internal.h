@@ -59,6 +59,8 @@ int launch_partial_valu(const PartialArgs& a, hipStream_t stream);
 // Launches on the matrix cores when an instantiation covers the shape
 // (bf16 queries, >= 16 query rows per KV head); *handled says whether it did.
 int launch_partial_mfma(const PartialArgs& a, hipStream_t stream, bool* handled);
+// Latent (MLA) pools, 576/512 head dims, bf16 queries, >= 64 query rows.
+int launch_partial_latent(const PartialArgs& a, hipStream_t stream, bool* handled);
 int valu_max_rows(int head_dim);
 // out_stride: output row i is written at row i * out_stride of v_out / lse_out
 int launch_merge(const float* v_in, const float* lse_in, int num_in, const int* o_indptr,

@@ -416,6 +416,7 @@ struct pdk_chunked_plan {
   struct {
     size_t ch_indptr, ch_indices, ch_len, ch_parts, ch_slots, ch_owner, req_chunks;
     size_t suf_indptr, suf_indices, suf_len, suf_parts, pair;
+    size_t all_req, all_row_ch, all_row_suf;  // one merge over every partial of a request
   } off{};
   const void* uploaded_to = nullptr;
 };
@@ -424,7 +425,7 @@ namespace {
 
 // byte offsets of the float regions behind the integer blob
 struct ChunkedLayout {
-  size_t v_pre, l_pre, v_suf, l_suf, v_ch, l_ch, v_pair, l_pair, total;
+  size_t v_pre, l_pre, v_suf, l_suf, v_ch, l_ch, v_pair, l_pair, v_all, l_all, total;
 };
 
 ChunkedLayout chunked_layout(const pdk_chunked_plan* p, int Hq, int Dv) {
@@ -443,6 +444,8 @@ ChunkedLayout chunked_layout(const pdk_chunked_plan* p, int Hq, int Dv) {
   L.l_ch = take((size_t)p->n_chunks * Hq, 1);
   L.v_pair = take((size_t)2 * p->batch * Hq, Dv);
   L.l_pair = take((size_t)2 * p->batch * Hq, 1);
+  L.v_all = take((size_t)(p->n_pre_parts + p->n_suf_parts) * Hq, Dv);
+  L.l_all = take((size_t)(p->n_pre_parts + p->n_suf_parts) * Hq, 1);
   L.total = o;
   return L;
 }
@@ -485,6 +488,16 @@ int pdk_chunked_plan_create(const pdk_csr* pre, int32_t P, int32_t C, int32_t S,
     suf_parts.push_back(suf_parts.back() + ceil_div(suf->kv_len[b], Ss));
   }
   for (int b = 0; b <= B; ++b) pair.push_back(2 * b);
+  // all partials of request b in one group: its chunk partitions, then its
+  // suffix partitions
+  std::vector<int32_t> all_req{0}, all_row_ch, all_row_suf;
+  for (int b = 0; b < B; ++b) {
+    const int base = all_req.back();
+    const int c0 = req_chunks[b], c1 = req_chunks[b + 1];
+    for (int k = c0; k < c1; ++k) all_row_ch.push_back(base + ch_parts[k] - ch_parts[c0]);
+    all_row_suf.push_back(base + ch_parts[c1] - ch_parts[c0]);
+    all_req.push_back(base + ch_parts[c1] - ch_parts[c0] + suf_parts[b + 1] - suf_parts[b]);
+  }
   plan->n_chunks = (int32_t)owner.size();
   plan->n_pre_parts = ch_parts.back();
   plan->n_suf_parts = suf_parts.back();
@@ -501,6 +514,9 @@ int pdk_chunked_plan_create(const pdk_csr* pre, int32_t P, int32_t C, int32_t S,
   plan->off.suf_len = bl.add(std::vector<int32_t>(suf->kv_len, suf->kv_len + B));
   plan->off.suf_parts = bl.add(suf_parts);
   plan->off.pair = bl.add(pair);
+  plan->off.all_req = bl.add(all_req);
+  plan->off.all_row_ch = bl.add(all_row_ch);
+  plan->off.all_row_suf = bl.add(all_row_suf);
   *plan_out = plan;
   return PDK_OK;
 }
@@ -558,6 +574,30 @@ int pdk_run_chunked_decode(const pdk_chunked_plan* plan, const pdk_kv_pool* pre_
   const int G = Hq / pre_pool->num_kv_heads;
   const int B = plan->batch;
   int st;
+  if (!chunk_out) {
+    // Without the per-chunk states: every partial of a request (chunk
+    // partitions, then suffix partitions) is merged by one launch. Merging
+    // is associative, so this equals merging within chunks, across chunks
+    // and with the suffix, up to f32 rounding.
+    float* v_all = (float*)(w + L.v_all);
+    float* l_all = (float*)(w + L.l_all);
+    if (plan->n_pre_parts > 0) {
+      pdk_csr vc{base + o.ch_indptr, base + o.ch_indices, base + o.ch_len, plan->n_chunks, 0};
+      st = partial_rows(pre_pool, &vc, q, q_dtype, Hq, sm_scale, plan->S, base + o.ch_parts,
+                        plan->n_pre_parts, base + o.ch_slots, base + o.ch_owner, 1, G,
+                        base + o.all_row_ch, v_all, l_all, stream);
+      if (st) return st;
+    }
+    if (plan->n_suf_parts > 0) {
+      pdk_csr vs{base + o.suf_indptr, base + o.suf_indices, base + o.suf_len, B, 0};
+      st = partial_rows(suf_pool, &vs, q, q_dtype, Hq, sm_scale, plan->Ss, base + o.suf_parts,
+                        plan->n_suf_parts, nullptr, nullptr, 0, G, base + o.all_row_suf, v_all,
+                        l_all, stream);
+      if (st) return st;
+    }
+    return merge_rows(v_all, l_all, plan->n_pre_parts + plan->n_suf_parts, base + o.all_req, B,
+                      Hq, Dv, out, lse_out, 1, stream);
+  }
   // chunk partials: each (request, chunk) is a view request with one member
   if (plan->n_pre_parts > 0) {
     pdk_csr vc{base + o.ch_indptr, base + o.ch_indices, base + o.ch_len, plan->n_chunks, 0};

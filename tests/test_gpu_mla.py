@@ -5,7 +5,10 @@ chunk states are LSE-merged, then merged with the new-token suffix state;
 
 Checked against the oracle's chunk states and against the plain definition
 (one softmax over prefix and suffix tokens), tolerance 5e-3 (fp8 KV after the
-identical dequant), LSE within 1e-4."""
+identical dequant), LSE within 1e-4. Without chunk outputs the library merges
+all partials of a request in one launch; that regrouping is checked against
+the staged merges to 1e-5 [cascade-PR, "How the #898 merge kernel is reused":
+merging is associative]."""
 import numpy as np
 import pytest
 import torch
@@ -17,7 +20,8 @@ from gpu_util import TOL, assert_close, assert_lse, to_device
 pytestmark = pytest.mark.gpu
 
 
-def run_chunked(pdk, share):
+def run_chunked(pdk, share, staged=True):
+    """staged: with per-chunk outputs (the staged merges); else one merge."""
     pre, suf = share.prefix, share.suffix
     p_pool, _, q = to_device(pre)
     s_pool, _, _ = to_device(suf)
@@ -27,6 +31,10 @@ def run_chunked(pdk, share):
                            suf.partition_tokens)
     counts = plan.counts()
     Hq, Dv = pre.num_q_heads, pre.head_dim_v
+    if not staged:
+        out, lse = plan.run(p_pool, s_pool, q, pre.sm_scale)
+        torch.cuda.synchronize()
+        return out.cpu().numpy(), lse.cpu().numpy(), None, None, counts
     chunk_out = torch.empty((counts["chunks"], Hq, Dv), dtype=torch.float32, device="cuda")
     chunk_lse = torch.empty((counts["chunks"], Hq), dtype=torch.float32, device="cuda")
     out, lse = plan.run(p_pool, s_pool, q, pre.sm_scale, chunk_out=chunk_out,
@@ -36,10 +44,12 @@ def run_chunked(pdk, share):
             chunk_lse.cpu().numpy(), counts)
 
 
-@pytest.mark.parametrize("context,chunk,part", [(2048, 1024, 512), (1000, 512, 256)])
-def test_mla_share_small(gpu, context, chunk, part):
+@pytest.mark.parametrize("context,chunk,part,spart", [(2048, 1024, 512, 64), (1000, 512, 256, 128),
+                                                     (4096, 4096, 2048, 64)])
+def test_mla_share_small(gpu, context, chunk, part, spart):
     share = W.mla_decode_share(seed=3005, batch=3, heads=128, context=context,
-                               suffix_tokens=100, chunk_tokens=chunk, partition_tokens=part)
+                               suffix_tokens=100, chunk_tokens=chunk, partition_tokens=part,
+                               suffix_partition_tokens=spart)
     out, lse, cout, clse, counts = run_chunked(gpu, share)
     assert counts["chunks"] == 3 * -(-context // chunk)
     ro, rl, rco, rcl = omla.mla_decode(share)
@@ -49,13 +59,19 @@ def test_mla_share_small(gpu, context, chunk, part):
     assert_lse(lse, rl, "lse")
     fo, fl = omla.mla_flat(share)
     assert_close(out, fo, TOL["fp8_e4m3"], "out vs one softmax")
+    # one merge over all partials of a request = the staged merges
+    o1, l1, _, _, _ = run_chunked(gpu, share, staged=False)
+    assert_close(o1, out, 1e-5, "single merge vs staged")
+    assert np.max(np.abs(l1 - lse)) <= 1e-5
 
 
 def test_mla_share_full_size_sampled(gpu):
     """Batch 32, 128 heads, 16384 cached fp8 tokens in 4096-token chunks plus
-    256 bf16 suffix tokens: sampled requests against the definition."""
+    256 bf16 suffix tokens, in the launch configuration the benchmark times
+    (2048-token partitions, 64-token suffix partitions, one merge): sampled
+    requests against the definition."""
     share = W.mla_decode_share()
-    out, lse, _, _, counts = run_chunked(gpu, share)
+    out, lse, _, _, counts = run_chunked(gpu, share, staged=False)
     assert counts["chunks"] == 32 * 4
     assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
     reqs = [0, 13, 31]

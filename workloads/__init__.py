@@ -313,11 +313,13 @@ class MlaShare:
 def mla_decode_share(seed: int = 1005, batch: int = 32, heads: int = 128,
                      context: int = 16384, suffix_tokens: int = 256,
                      chunk_tokens: int = 4096, page_size: int = 64,
-                     partition_tokens: int = 1024, poison: bool = True) -> MlaShare:
+                     partition_tokens: int = 2048, suffix_partition_tokens: int = 64,
+                     poison: bool = True) -> MlaShare:
     """MLA-shaped share: 128 query heads, 1 latent KV head, K dim 576
     (512 latent + 64 rope), V = first 512 dims; cached prefix in an fp8
     e4m3 pool (per-tensor scale amax/448) of page 64; suffix in a bf16 pool
-    of page 64; bf16 queries; scale 1/sqrt(576)."""
+    of page 64; bf16 queries; scale 1/sqrt(576). Partition sizes are launch
+    parameters (whole pages), not part of the data."""
     rng = np.random.default_rng(seed)
     Dk, Dv = 576, 512
     npg = _pages(context, page_size)
@@ -332,7 +334,7 @@ def mla_decode_share(seed: int = 1005, batch: int = 32, heads: int = 128,
     suffix = paged_batch_from_lists("mla_suffix_bf16", rng, slists, [suffix_tokens] * batch,
                                     page_size=page_size, num_q_heads=heads, num_kv_heads=1,
                                     head_dim_k=Dk, head_dim_v=Dv, kv_dtype="bf16",
-                                    q_dtype="bf16", partition_tokens=spg * page_size,
+                                    q_dtype="bf16", partition_tokens=suffix_partition_tokens,
                                     pad_blocks=4, latent=True, poison=poison)
     suffix.q = prefix.q  # one query token per sequence, shared by both ranges
     return MlaShare(prefix=prefix, suffix=suffix, chunk_tokens=chunk_tokens)
