@@ -324,10 +324,10 @@ def bench_cascade_arms(args, torch, pdk, W, dev):
     for name, params in (
             ("flat", pdk.CascadeParams(enabled=0, l1_partition_tokens=512)),
             ("cascade_single_group", pdk.CascadeParams(enabled=1, max_groups=1,
-                                                       l0_partition_tokens=256,
+                                                       l0_partition_tokens=512,
                                                        l1_partition_tokens=512)),
             ("cascade_all_groups", pdk.CascadeParams(enabled=1, max_groups=0,
-                                                     l0_partition_tokens=256,
+                                                     l0_partition_tokens=512,
                                                      l1_partition_tokens=512))):
         plan, plan_us = planned(torch, pdk, b, params, dev)
         wall_ms, t_part, t_merge = run_plan_steps(args, torch, pdk, b, pool, q, plan, dev)

@@ -36,6 +36,7 @@ int fail(int status, const char* fmt, ...) {
   return status;
 }
 
+
 static int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -156,6 +157,8 @@ int merge_rows(const float* v_in, const float* lse_in, int num_in, const int* o_
 int launch_partial(const PartialArgs& a, hipStream_t stream) {
   bool handled = false;
   int st = launch_partial_latent(a, stream, &handled);
+  if (st || handled) return st;
+  st = launch_partial_dma(a, stream, &handled);
   if (st || handled) return st;
   st = launch_partial_mfma(a, stream, &handled);
   if (st || handled) return st;

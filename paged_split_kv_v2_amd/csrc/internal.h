@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+
 #include "pdk.h"
 
 namespace pdk {
@@ -61,6 +62,9 @@ int launch_partial_valu(const PartialArgs& a, hipStream_t stream);
 int launch_partial_mfma(const PartialArgs& a, hipStream_t stream, bool* handled);
 // Latent (MLA) pools, 576/512 head dims, bf16 queries, >= 64 query rows.
 int launch_partial_latent(const PartialArgs& a, hipStream_t stream, bool* handled);
+// bf16 K/V pools of head dim 128 with bf16 queries, K/V staged by
+// global->LDS loads, products on the matrix cores.
+int launch_partial_dma(const PartialArgs& a, hipStream_t stream, bool* handled);
 int valu_max_rows(int head_dim);
 // out_stride: output row i is written at row i * out_stride of v_out / lse_out
 int launch_merge(const float* v_in, const float* lse_in, int num_in, const int* o_indptr,
@@ -88,5 +92,6 @@ int launch_dequant(const uint8_t* in, long long n, float scale, uint16_t* out,
 
 // error reporting (thread-local message, see pdk_last_error)
 int fail(int status, const char* fmt, ...);
+
 
 }  // namespace pdk
