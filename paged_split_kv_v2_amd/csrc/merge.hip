@@ -10,7 +10,9 @@
 // laid out for HBM: each thread owns four consecutive floats of one output
 // row (one 16-byte load per input row), a one-wave workgroup covers 256
 // floats of the [H, D] row, and a group's input rows are read eight at a
-// time so that eight independent 16-byte loads per thread are in flight.
+// time (their LSEs and 16-byte value loads issued together) and folded in
+// with a running maximum, so a group costs one memory round trip per eight
+// rows.
 
 #include "device.h"
 #include "internal.h"
@@ -47,33 +49,44 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
     out = *reinterpret_cast<const float4*>(v_in + (size_t)a * HD + e);
     lse = lse0;
   } else if (n > 1) {
-    float m = -INFINITY;
-    for (int r = 0; r < n; ++r) m = fmaxf(m, lrow[(size_t)r * H]);
-    if (m != -INFINITY) {
-      float l = 0.f;
-      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-      const float4* vrow = reinterpret_cast<const float4*>(v_in + (size_t)a * HD + e);
-      const size_t vstep = (size_t)HD / 4;
-      for (int r0 = 0; r0 < n; r0 += kMergeBatch) {
-        float w[kMergeBatch];
-        float4 x[kMergeBatch];
+    // one pass in batches of kMergeBatch rows: the batch's LSEs and value
+    // rows are loaded together, then folded in with a running maximum (for
+    // groups of at most kMergeBatch rows this is the plain two-step merge)
+    float m = -INFINITY, l = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4* vrow = reinterpret_cast<const float4*>(v_in + (size_t)a * HD + e);
+    const size_t vstep = (size_t)HD / 4;
+    for (int r0 = 0; r0 < n; r0 += kMergeBatch) {
+      float w[kMergeBatch];
+      float4 x[kMergeBatch];
 #pragma unroll
-        for (int k = 0; k < kMergeBatch; ++k) {
-          const bool in = r0 + k < n;
-          w[k] = in ? lrow[(size_t)(r0 + k) * H] : -INFINITY;
-          x[k] = in ? vrow[(size_t)(r0 + k) * vstep] : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-#pragma unroll
-        for (int k = 0; k < kMergeBatch; ++k) {
-          if (w[k] == -INFINITY) continue;  // empty state: not read into the sum
-          const float wk = fast_exp2(w[k] - m);
-          l += wk;
-          acc.x = fmaf(wk, x[k].x, acc.x);
-          acc.y = fmaf(wk, x[k].y, acc.y);
-          acc.z = fmaf(wk, x[k].z, acc.z);
-          acc.w = fmaf(wk, x[k].w, acc.w);
-        }
+      for (int k = 0; k < kMergeBatch; ++k) {
+        const bool in = r0 + k < n;
+        w[k] = in ? lrow[(size_t)(r0 + k) * H] : -INFINITY;
+        x[k] = in ? vrow[(size_t)(r0 + k) * vstep] : make_float4(0.f, 0.f, 0.f, 0.f);
       }
+      float bm = w[0];
+#pragma unroll
+      for (int k = 1; k < kMergeBatch; ++k) bm = fmaxf(bm, w[k]);
+      if (bm == -INFINITY) continue;  // only empty states in this batch
+      if (bm > m) {
+        const float c = (m == -INFINITY) ? 0.f : fast_exp2(m - bm);
+        l *= c;
+        acc = make_float4(acc.x * c, acc.y * c, acc.z * c, acc.w * c);
+        m = bm;
+      }
+#pragma unroll
+      for (int k = 0; k < kMergeBatch; ++k) {
+        if (w[k] == -INFINITY) continue;  // empty state: not read into the sum
+        const float wk = fast_exp2(w[k] - m);
+        l += wk;
+        acc.x = fmaf(wk, x[k].x, acc.x);
+        acc.y = fmaf(wk, x[k].y, acc.y);
+        acc.z = fmaf(wk, x[k].z, acc.z);
+        acc.w = fmaf(wk, x[k].w, acc.w);
+      }
+    }
+    if (m != -INFINITY) {
       out = make_float4(acc.x / l, acc.y / l, acc.z / l, acc.w / l);
       lse = m + log2f(l);
     }
