@@ -180,17 +180,29 @@ def bench_flat(args, torch, pdk, W, dev):
     return res
 
 
+def kernel_source_sha(kernel_source):
+    """sha256 over the kernel's translation unit and the shared headers it
+    includes (device.h, internal.h), in that order."""
+    import hashlib
+    csrc = os.path.join(ROOT, "paged_split_kv_v2_amd", "csrc")
+    h = hashlib.sha256()
+    for name in (kernel_source, "device.h", "internal.h"):
+        path = os.path.join(csrc, name)
+        if not os.path.exists(path):
+            return None
+        h.update(open(path, "rb").read())
+    return h.hexdigest()
+
+
 def traffic_record(kernel_source, launches_per_step=1):
     """HBM bytes per launch from the committed rocprofv3 counter record,
-    or None when the kernel source has changed since it was taken."""
-    import hashlib
+    or None when the kernel's sources have changed since it was taken."""
     rec_path = os.path.join(ROOT, "profiles", "traffic.json")
-    src_path = os.path.join(ROOT, "paged_split_kv_v2_amd", "csrc", kernel_source)
-    if not (os.path.exists(rec_path) and os.path.exists(src_path)):
+    if not os.path.exists(rec_path):
         return None
     rec = json.load(open(rec_path)).get(kernel_source)
-    sha = hashlib.sha256(open(src_path, "rb").read()).hexdigest()
-    if not rec or rec.get("source_sha256") != sha:
+    sha = kernel_source_sha(kernel_source)
+    if not rec or sha is None or rec.get("source_sha256") != sha:
         return None
     return int(rec["fetch_kib_per_dispatch"] * 1024 * rec["fetch_factor"] +
                rec["write_kib_per_dispatch"] * 1024 * rec["write_factor"])
