@@ -70,17 +70,24 @@ class Timer:
 
 
 def time_steps(torch, parts, steps, warmup):
-    """Exactly `steps` steps, synchronized on both sides; each step runs the
-    callables in `parts` in order with an event between consecutive ones.
-    Returns the wall time per step (ms) and the mean device time of each
-    part (us), measured by the events."""
+    """Exactly `steps` steps, synchronized on both sides, each step running
+    the callables in `parts` in order with nothing else enqueued between them
+    (a timing event between two launches costs several microseconds on this
+    part). Then the same number of steps again with an event before and
+    after every part, for the mean device time of each part. Returns the wall
+    time per step of the first run (ms) and those device times (us)."""
     for _ in range(warmup):
         for f in parts:
             f()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        for f in parts:
+            f()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1000.0 / steps
     timer = Timer(torch)
     spans = [[] for _ in parts]
-    t0 = time.perf_counter()
     for _ in range(steps):
         a = timer.mark()
         for i, f in enumerate(parts):
@@ -89,7 +96,6 @@ def time_steps(torch, parts, steps, warmup):
             spans[i].append((a, b))
             a = b
     torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1000.0 / steps
     return wall_ms, [timer.mean_us(sp) for sp in spans]
 
 
