@@ -78,3 +78,29 @@ def test_mla_share_full_size_sampled(gpu):
     fo, fl = omla.mla_flat(share, requests=reqs)
     assert_close(out[reqs], fo[reqs], TOL["fp8_e4m3"], "out")
     assert_lse(lse[reqs], fl[reqs], "lse")
+
+
+def test_mla_ragged_and_empty_suffix(gpu):
+    """Contexts shorter than one chunk, not a multiple of the tile or page,
+    and requests whose new-token suffix is empty (their state is the prefix
+    state alone)."""
+    pre_lens, suf_lens = [100, 1024 + 37, 64, 5], [0, 70, 128, 0]
+    pre = W.random_batch(3101, batch=4, page_size=64, num_q_heads=128, num_kv_heads=1,
+                         head_dim=576, head_dim_v=512, kv_dtype="fp8_e4m3", q_dtype="bf16",
+                         min_len=0, max_len=0, partition_tokens=256, lens=pre_lens, latent=True)
+    suf = W.random_batch(3102, batch=4, page_size=64, num_q_heads=128, num_kv_heads=1,
+                         head_dim=576, head_dim_v=512, kv_dtype="bf16", q_dtype="bf16",
+                         min_len=0, max_len=0, partition_tokens=64, lens=suf_lens, latent=True)
+    suf.q = pre.q
+    suf.sm_scale = pre.sm_scale
+    share = W.MlaShare(prefix=pre, suffix=suf, chunk_tokens=512)
+    out, lse, cout, clse, counts = run_chunked(gpu, share)
+    ro, rl, rco, rcl = omla.mla_decode(share)
+    assert_close(cout, rco, TOL["fp8_e4m3"], "chunk out")
+    assert_lse(clse, rcl, "chunk lse")
+    assert_close(out, ro, TOL["fp8_e4m3"], "out")
+    assert_lse(lse, rl, "lse")
+    fo, fl = omla.mla_flat(share)
+    assert_close(out, fo, TOL["fp8_e4m3"], "out vs one softmax")
+    o1, l1, _, _, _ = run_chunked(gpu, share, staged=False)
+    assert_close(o1, out, 1e-5, "single merge vs staged")

@@ -111,3 +111,17 @@ def test_deterministic(gpu):
     o1, l1, _ = flat_decode(b, pool, csr, q)
     o2, l2, _ = flat_decode(b, pool, csr, q)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("page_size", [4, 8, 32, 64])
+def test_stacked_rows_page_sizes(gpu, page_size):
+    """More than 16 query rows per KV head (the LDS-ring matrix-core path)
+    with other page sizes: lengths around page, tile (32 tokens) and
+    partition boundaries, one empty request."""
+    S = 4 * max(page_size, 32)
+    lens = [1, page_size - 1, page_size + 1, 31, 32, 33, S - 1, S, S + 1, 2 * S + 5, 0, 97]
+    lens = [max(0, x) for x in lens]
+    b = W.random_batch(80 + page_size, batch=len(lens), page_size=page_size, num_q_heads=64,
+                       num_kv_heads=2, head_dim=128, kv_dtype="bf16", q_dtype="bf16",
+                       min_len=0, max_len=0, partition_tokens=S, lens=lens)
+    check_partials_and_flat(gpu, b)
