@@ -7,39 +7,32 @@
 // contract as the other partial kernels: one normalized partial and its log2
 // LSE per (request, partition, query row).
 //
-// Workgroup = 4 waves, 64 query rows; two workgroups share a CU (two waves
-// per SIMD), so one computes while the other waits at a barrier or on LDS.
-// Waves w and w^2 share rows [32(w%2), 32(w%2)+32) for the whole partition
-// and split the work on them in halves:
-//   * S^T: wave half hf contracts the 16-dim k-steps 2ks + hf (ks < 18) with
-//     its half of Q^T held as B operands of v_mfma_f32_32x32x16_bf16 (18
-//     k-steps x 8 bf16 per lane); the two partial sums are exchanged through
-//     LDS and added, so both waves hold the same S^T (IEEE addition
-//     commutes);
-//   * O^T: wave half hf accumulates value dims [256hf, 256hf+256) as 8
-//     accumulator blocks of 32x32 (128 registers per lane);
+// Workgroup = 8 waves (two per SIMD), 128 query rows; wave w owns rows
+// [16w, 16w+16) for the whole partition:
+//   * Q^T as B operands of v_mfma_f32_16x16x32_bf16 (18 k-steps x 8 bf16 per
+//     lane) and O^T = 512 dims x 16 rows as 32 accumulator blocks of 16x16
+//     (128 registers per lane); no exchange between waves;
 //   * the tile (32 tokens) is staged in LDS as bf16 [token][576] (fp8 rows
 //     dequantized on the way: RNE_bf16(f32(x) * scale)); 16-byte chunks are
 //     XOR-swizzled by token so that both reads below are free of bank
 //     conflicts;
-//   * S^T = K . Q^T: A = 32 K rows read with 16-byte loads;
-//   * O^T += V^T . P^T: A = 32 value dims x 16 tokens read straight from the
+//   * S^T = K . Q^T: A = 16 K rows read with 16-byte loads (two 16-token
+//     blocks per tile);
+//   * O^T += V^T . P^T: A = 16 value dims x 32 tokens read straight from the
 //     row-major tile with the gfx950 transposing LDS load (ds_read_b64_tr_b16:
 //     in each group of 16 lanes, lane i receives element i%4 of the 8 bytes
 //     addressed by lane 4e + i/4 as its element e), no transposed copy; B =
 //     P^T taken from the S^T accumulators as they lie (the MFMA's k slots of
-//     lane half h are the tokens {4h..4h+3, 8+4h..8+4h+3} of each 16-token
-//     block, and the V^T loads use the same token order);
+//     lane group q are the tokens {4q..4q+3} and {16+4q..16+4q+3}, and the V^T
+//     loads use the same token order);
 //   * online softmax per query row in log2 units, lazy reference maximum as
 //     in the other kernels; P is rounded to bf16 for the PV product.
-// The next tile's rows are fetched with gfx950's global->LDS loads (16 bytes
-// per lane, placed at base + 16*lane) into a raw staging buffer before the
-// products of the current tile; after them each lane converts the 16 bytes
-// it fetched itself into the tile buffer, so no registers hold rows in
-// flight. Three barriers per tile: S^T exchange, tile buffer free, tile
-// buffer filled. The two row halves of a partition are issued 8 blocks apart,
-// which lands them on the same XCD (blocks are dealt round-robin to the 8
-// XCDs) at about the same time: the second reads the rows from that L2.
+// Pipeline: two bf16 tile buffers and one raw staging buffer. While tile i
+// is multiplied from one buffer, tile i + 1 (fetched during tile i - 1 by
+// gfx950's global->LDS loads, 16 bytes per lane at base + 16*lane) is
+// dequantized into the other by the lanes that fetched its bytes, and tile
+// i + 2 is then fetched; one barrier per tile. No registers hold rows in
+// flight.
 
 #include "device.h"
 #include "internal.h"
@@ -49,7 +42,7 @@ namespace pdk {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -57,8 +50,8 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 enum { LK_BF16 = 1, LK_FP8 = 2 };
 constexpr int kTT = 32;          // tokens per tile
-constexpr int kWaves = 4;
-constexpr int kRows = 64;
+constexpr int kWaves = 8;
+constexpr int kRows = 128;
 constexpr int kMaxPagesL = 256;  // pages of one partition (plus one)
 constexpr float kLazyL = 8.f;
 
@@ -85,11 +78,11 @@ __device__ __forceinline__ void lds_barrier() {
 enum : int { SG_MFMA = 0x008, SG_DS_READ = 0x100 };
 
 template <int DK, int DV, int KT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void partial_latent_kernel(const PartialArgs a) {
   constexpr int NT = 64 * kWaves;
-  constexpr int KS = DK / 32;                       // k-steps of S^T per contraction half
-  constexpr int DB = DV / 64;                       // 32-dim output blocks per value half
+  constexpr int KS = DK / 32;                       // k-steps of S^T (32 dims)
+  constexpr int DB = DV / 16;                       // 16-dim output blocks
   constexpr int ESZ = (KT == LK_FP8) ? 1 : 2;
   constexpr int RCH = DK * ESZ / 16;                // 16-byte stored chunks per token
   constexpr int ITEMS = kTT * RCH;
@@ -97,18 +90,18 @@ void partial_latent_kernel(const PartialArgs a) {
   static_assert(ITEMS % 64 == 0, "whole blocks");
   static_assert(DK % 64 == 0 && DV % 32 == 0 && DV <= DK, "latent shapes");
 
-  __shared__ __align__(16) uint16_t sk[kTT * DK];
+  __shared__ __align__(16) uint16_t sk0[kTT * DK];
+  __shared__ __align__(16) uint16_t sk1[kTT * DK];
   __shared__ __align__(16) u32x4_t sraw[ITEMS];         // fetched rows, item order
-  __shared__ __align__(16) u32x4_t xs[kWaves][4][64];  // partial S^T of each wave
   __shared__ int sm_pid[kMaxPagesL];
 
   // block -> (unit = partition * Hkv + kv head, row tile): the row tiles of a
   // unit are 8 blocks apart, 8 units per group
   const int n_tiles = (a.max_rows + kRows - 1) / kRows;
   const int bid = blockIdx.x;
-  const int unit = 8 * (bid / (8 * n_tiles)) + (bid & 7);
-  const int tile = (bid >> 3) % n_tiles;
-  if (unit >= a.num_parts * a.Hkv) return;  // uniform: padding of the last group
+  const int unit = bid / n_tiles;
+  const int tile = bid - unit * n_tiles;
+  if (unit >= a.num_parts * a.Hkv) return;  // uniform; the grid has no padding
   const int h = unit % a.Hkv;
   const int r = unit / a.Hkv;
   const int tid = threadIdx.x;
@@ -151,14 +144,13 @@ void partial_latent_kernel(const PartialArgs a) {
 
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int hl = lane >> 5;   // lane half
-  const int c32 = lane & 31;  // MFMA column (query row) / A row
-  const int hf = wave >> 1;   // contraction half of S^T, value half of O^T
+  const int q4 = lane >> 4;   // lane group
+  const int r16 = lane & 15;  // query row of the wave / MFMA column
 
-  // half of the 32 query rows as B fragments: lane -> row c32,
-  // dims 16(2ks + hf) + 8hl + i
+  // the wave's 16 query rows as B fragments of v_mfma_f32_16x16x32_bf16:
+  // lane -> row r16, dims 32ks + 8q4 + i
   u32x4_t qf[KS];
-  const int my_row = row0 + 32 * (wave & 1) + c32;
+  const int my_row = row0 + 16 * wave + r16;
   {
     int qb = b, head = 0;
     const bool live = my_row < nrows;
@@ -169,7 +161,7 @@ void partial_latent_kernel(const PartialArgs a) {
     }
     // row 0 of request qb stands in for padding rows: always a valid address
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
-                         ((size_t)qb * a.Hq + head) * DK + 16 * hf + 8 * hl;
+                         ((size_t)qb * a.Hq + head) * DK + 8 * q4;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const u32x4_t x = *reinterpret_cast<const u32x4_t*>(qp + 32 * ks);
@@ -198,13 +190,22 @@ void partial_latent_kernel(const PartialArgs a) {
                                        16, 0, 0);
     }
   };
-  auto convert_tile = [&]() {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's fetches have landed
-    for (int k = wave; k < NBLK; k += kWaves) {
-      const int c = 64 * k + lane;
+  // every wave converts NIT items (waves with fewer repeat their last one:
+  // same bytes to the same place), so the code is branch-free and can be
+  // interleaved with the products of the current tile
+  constexpr int NIT = (NBLK + kWaves - 1) / kWaves;
+  auto convert_tile = [&](uint16_t* dstbuf) {
+    // recomputed per tile rather than kept live across it
+    int lane_r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(lane_r) : "v"(lane));
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      int k = wave + kWaves * it;
+      k = (k < NBLK) ? k : k - kWaves;
+      const int c = 64 * k + lane_r;
       const int tt = c / RCH, rc = c - tt * RCH;
       const u32x4_t x = sraw[c];
-      uint16_t* row = &sk[tt * DK];
+      uint16_t* row = dstbuf + tt * DK;
       if constexpr (KT == LK_FP8) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {  // 8 codes -> one 16-byte bf16 chunk
@@ -219,105 +220,98 @@ void partial_latent_kernel(const PartialArgs a) {
     }
   };
 
-  f32x16_t acc[DB];
+  f32x4_t acc[DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) acc[db][j] = 0.f;
+  for (int db = 0; db < DB; ++db) acc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float run_m = -INFINITY, run_l = 0.f;
 
-  // Per-lane LDS element offsets within a tile buffer. The swizzle only
-  // permutes the low three bits of the chunk index, so each read below is a
-  // per-lane base plus a compile-time offset:
-  //   K fragment of k-step 2ks + hf: row c32, chunk 4ks + 2hf + hl
-  //     -> c32*DK + 64(ks/2) + 8((2hf + hl) ^ f(c32) ^ 4(ks%2));
-  //   V^T fragment (kb, rho, db): token 16kb + 8rho + tr_tok, dims
-  //     (DV/2)hf + 32db + tr_dim -> chunk 32hf + 4db + e with e = tr_dim/8,
-  //     swizzled by f(t) = y ^ 4rho, y = 5(tr_tok/2) mod 8.
-  const int fk = (5 * (c32 >> 1)) & 7;
-  const int kofs0 = c32 * DK + 8 * ((2 * hf + hl) ^ fk);
-  const int kofs1 = c32 * DK + 8 * ((2 * hf + hl) ^ fk ^ 4);
-  const int tr_tok = 4 * hl + ((lane & 15) >> 2);
-  const int tr_e = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-  const int tr_z = tr_e ^ ((5 * (tr_tok >> 1)) & 7);
-  const int vbase = tr_tok * DK + (DV / 2) * hf + 4 * (lane & 1);
-  const int vofs0 = vbase + 8 * tr_z;
-  const int vofs1 = vbase + 8 * (tr_z ^ 4);
+  // Per-lane LDS element offsets within the tile. The swizzle permutes the
+  // low three bits of the chunk index, so each read is a per-lane base plus
+  // a compile-time offset:
+  //   K fragment (tb, ks): token 16tb + r16, chunk 4ks + q4
+  //     -> (16tb + r16)*DK + 64(ks/2) + 8(q4 ^ f(r16) ^ 4(ks%2));
+  //   V^T fragment of dims 16db..16db+15: tokens 4q4 + e and 16 + 4q4 + e,
+  //     lane r16 of the group addressing token 4q4 + r16/4 at dims
+  //     16db + 4(r16%4), chunk 2db + (r16%4)/2
+  //     -> tok*DK + 64(db/4) + 8((2(db%4)) ^ z) + 4(r16%2), z = (r16%4)/2 ^ f(tok).
+  const int fk = (5 * (r16 >> 1)) & 7;
+  const int kofs0 = r16 * DK + 8 * (q4 ^ fk);
+  const int kofs1 = r16 * DK + 8 * (q4 ^ fk ^ 4);
+  const int v_tok = 4 * q4 + (r16 >> 2);
+  const int v_z = ((r16 & 3) >> 1) ^ ((5 * (v_tok >> 1)) & 7);
+  int vofs[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) vofs[c] = v_tok * DK + 8 * ((2 * c) ^ v_z) + 4 * (r16 & 1);
 
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the query fragments have landed
   __syncthreads();                     // page ids visible
-  if (start < end) {
+  const int n_tt = (end > start) ? (end - start + kTT - 1) / kTT : 0;
+  if (n_tt > 0) {
     fetch_tile(start);
-    convert_tile();
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    convert_tile(sk0);
+    if (n_tt > 1) fetch_tile(start + kTT);
   }
   __syncthreads();
-  for (int t0 = start; t0 < end; t0 += kTT) {
-    const bool more = t0 + kTT < end;  // uniform
-    const uint16_t* tile_k = sk;
 
-    // S^T = K . Q^T: lane -> query row c32, tokens 8(j/4) + 4hl + j%4
-    f32x16_t s;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) s[j] = 0.f;
+  // tile i is read from buffer i % 2 while tile i + 1 is converted into the
+  // other one (its rows fetched during tile i - 1) and tile i + 2 fetched
+  auto run_tile = [&](int i, const uint16_t* tile_k, uint16_t* next_buf) {
+    const int t0 = start + i * kTT;
+    // S^T = K . Q^T: block tb, lane -> query row r16, tokens 16tb + 4q4 + j
+    f32x4_t s[2];
     {
-      // K fragments are read KP k-steps ahead of their product
-      constexpr int KP = 2;
-      u32x4_t kf[KS];
-      auto kread = [&](int ks) {
-        return *reinterpret_cast<const u32x4_t*>(tile_k + ((ks & 1) ? kofs1 : kofs0) +
-                                                 64 * (ks >> 1));
+      constexpr int KP = 2, NK = 2 * KS;
+      u32x4_t kf[NK];
+      auto kread = [&](int i) {
+        const int tb = i / KS, ks = i - tb * KS;
+        return *reinterpret_cast<const u32x4_t*>(tile_k + 16 * tb * DK +
+                                                 ((ks & 1) ? kofs1 : kofs0) + 64 * (ks >> 1));
       };
+      s[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      s[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KP; ++ks) kf[ks] = kread(ks);
+      for (int i = 0; i < KP; ++i) kf[i] = kread(i);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if (ks + KP < KS) kf[ks + KP] = kread(ks + KP);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[ks]), as_bf16x8(qf[ks]), s, 0,
-                                                    0, 0);
+      for (int i = 0; i < NK; ++i) {
+        if (i + KP < NK) kf[i + KP] = kread(i + KP);
+        const int tb = i / KS, ks = i - tb * KS;
+        s[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[i]), as_bf16x8(qf[ks]), s[tb],
+                                                        0, 0, 0);
       }
       __builtin_amdgcn_sched_group_barrier(SG_DS_READ, KP, 0);
 #pragma unroll
-      for (int i = 0; i < KS - KP; ++i) {
+      for (int i = 0; i < NK - KP; ++i) {
         __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
         __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
       }
       __builtin_amdgcn_sched_group_barrier(SG_MFMA, KP, 0);
     }
-    if (more) fetch_tile(t0 + kTT);
-    // exchange the partial sums with the other half
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      xs[wave][q][lane] = u32x4_t{f32_bits(s[4 * q]), f32_bits(s[4 * q + 1]),
-                                  f32_bits(s[4 * q + 2]), f32_bits(s[4 * q + 3])};
-    lds_barrier();
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const u32x4_t o = xs[wave ^ 2][q][lane];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s[4 * q + i] += bits_f32(o[i]);
-    }
 
-    // row max over the two lane halves, in scaled log2 units; a full tile
+    // row max over the four lane groups, in scaled log2 units; a full tile
     // scales inside the exponent below, the last tile masks first
     float cs = a.scale_log2, mx;
     if (t0 + kTT <= end) {
-      float hi = fmaxf(s[0], s[1]), lo = fminf(s[0], s[1]);
+      float hi = fmaxf(s[0][0], s[1][0]), lo = fminf(s[0][0], s[1][0]);
 #pragma unroll
-      for (int j = 2; j < 16; j += 2) {
-        hi = fmaxf(hi, fmaxf(s[j], s[j + 1]));
-        lo = fminf(lo, fminf(s[j], s[j + 1]));
+      for (int j = 1; j < 4; ++j) {
+        hi = fmaxf(hi, fmaxf(s[0][j], s[1][j]));
+        lo = fminf(lo, fminf(s[0][j], s[1][j]));
       }
       mx = (cs >= 0.f ? hi : lo) * cs;
     } else {
       mx = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int t = t0 + 8 * (j >> 2) + 4 * hl + (j & 3);
-        s[j] = (t < end) ? s[j] * cs : -INFINITY;
-        mx = fmaxf(mx, s[j]);
-      }
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int t = t0 + 16 * tb + 4 * q4 + j;
+          s[tb][j] = (t < end) ? s[tb][j] * cs : -INFINITY;
+          mx = fmaxf(mx, s[tb][j]);
+        }
       cs = 1.f;
     }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
     {
       const auto sw = __builtin_amdgcn_permlane32_swap(f32_bits(mx), f32_bits(mx), false, false);
       mx = fmaxf(bits_f32(sw[0]), bits_f32(sw[1]));  // max over lanes l and l ^ 32
@@ -332,74 +326,74 @@ void partial_latent_kernel(const PartialArgs a) {
       run_m = mn;
     }
     const float mu = (run_m == -INFINITY) ? 0.f : run_m;
-    uint32_t pw[8];
+    // P^T as the B operand: k slots 8q4 + i are tokens 4q4 + i (i < 4) and
+    // 16 + 4q4 + i - 4
+    uint32_t pw[4];
 #pragma unroll
-    for (int j = 0; j < 16; j += 2) {
-      const float p0 = fast_exp2(__builtin_fmaf(s[j], cs, -mu));
-      const float p1 = fast_exp2(__builtin_fmaf(s[j + 1], cs, -mu));
-      run_l += p0 + p1;
-      pw[j >> 1] = pack_bf16x2_rne(p0, p1);
-    }
-    const bf16x8_t pb0 = as_bf16x8(u32x4_t{pw[0], pw[1], pw[2], pw[3]});
-    const bf16x8_t pb1 = as_bf16x8(u32x4_t{pw[4], pw[5], pw[6], pw[7]});
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int j = 0; j < 4; j += 2) {
+        const float p0 = fast_exp2(__builtin_fmaf(s[tb][j], cs, -mu));
+        const float p1 = fast_exp2(__builtin_fmaf(s[tb][j + 1], cs, -mu));
+        run_l += p0 + p1;
+        pw[2 * tb + (j >> 1)] = pack_bf16x2_rne(p0, p1);
+      }
+    const bf16x8_t pb = as_bf16x8(u32x4_t{pw[0], pw[1], pw[2], pw[3]});
 
+    if (i + 1 < n_tt) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile i + 1 has landed
+      convert_tile(next_buf);
+    }
     // O^T += V^T . P^T, V^T fragments by transposing loads issued VP
-    // products ahead; step i = (db, kb) = (i / 2, i % 2)
+    // products ahead
     {
-      constexpr int NS = 2 * DB, VP = 1;
-      u32x4_t vf[NS];
-      auto vread = [&](int i) {
-        const int db = i >> 1, kb = i & 1;
-        s16x4_t v[2];
-#pragma unroll
-        for (int rho = 0; rho < 2; ++rho) {
-          const uint16_t* ptr = tile_k + (((db & 1) ^ rho) ? vofs1 : vofs0) +
-                                (16 * kb + 8 * rho) * DK + 64 * (db >> 1);
-          v[rho] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)ptr);
-        }
-        const u32x2_t v0 = __builtin_bit_cast(u32x2_t, v[0]), v1 = __builtin_bit_cast(u32x2_t, v[1]);
+      constexpr int VP = 2;
+      u32x4_t vf[DB];
+      auto vread = [&](int db) {
+        const uint16_t* p0 = tile_k + vofs[db & 3] + 64 * (db >> 2);
+        const u32x2_t v0 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p0));
+        const u32x2_t v1 =
+            __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p0 + 16 * DK)));
         return u32x4_t{v0[0], v0[1], v1[0], v1[1]};
       };
 #pragma unroll
       for (int i = 0; i < VP; ++i) vf[i] = vread(i);
 #pragma unroll
-      for (int i = 0; i < NS; ++i) {
-        if (i + VP < NS) vf[i + VP] = vread(i + VP);
-        acc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf[i]), (i & 1) ? pb1 : pb0,
-                                                              acc[i >> 1], 0, 0, 0);
+      for (int db = 0; db < DB; ++db) {
+        if (db + VP < DB) vf[db + VP] = vread(db + VP);
+        acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vf[db]), pb, acc[db], 0, 0, 0);
       }
       __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2 * VP, 0);
 #pragma unroll
-      for (int i = 0; i < NS - VP; ++i) {
+      for (int i = 0; i < DB - VP; ++i) {
         __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
         __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
       }
       __builtin_amdgcn_sched_group_barrier(SG_MFMA, VP, 0);
     }
-    if (more) {
-      lds_barrier();  // every wave is done with the tile buffer
-      convert_tile();
-    }
-    lds_barrier();  // next tile staged; exchange slots free again
+    if (i + 2 < n_tt) fetch_tile(t0 + 2 * kTT);
+    lds_barrier();  // tile i read by all waves; tile i + 1 staged
+  };
+  for (int i = 0; i < n_tt; i += 2) {
+    run_tile(i, sk0, sk1);
+    if (i + 1 < n_tt) run_tile(i + 1, sk1, sk0);
   }
 
-  // row sum over the lane halves, normalized partial and its LSE
+  // row sum over the lane groups, normalized partial and its LSE
   float l = run_l;
+  l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
   if (my_row < nrows) {
     const int m = my_row / a.G, g = my_row % a.G;
     const int orow = (stacked ? a.out_row_base[mbase + m] : a.out_row_base[b]) + p;
     const size_t o = (size_t)orow * a.Hq + h * a.G + g;
-    float* dst = a.v_out + o * DV + (DV / 2) * hf + 4 * hl;
+    float* dst = a.v_out + o * DV + 4 * q4;
     const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int jb = 0; jb < 4; ++jb)
-        *reinterpret_cast<float4*>(dst + 32 * db + 8 * jb) =
-            make_float4(acc[db][4 * jb] * inv, acc[db][4 * jb + 1] * inv,
-                        acc[db][4 * jb + 2] * inv, acc[db][4 * jb + 3] * inv);
-    if (hl == 0 && hf == 0) a.lse_out[o] = (l > 0.f) ? run_m + log2f(l) : -INFINITY;
+      *reinterpret_cast<float4*>(dst + 16 * db) =
+          make_float4(acc[db][0] * inv, acc[db][1] * inv, acc[db][2] * inv, acc[db][3] * inv);
+    if (q4 == 0) a.lse_out[o] = (l > 0.f) ? run_m + log2f(l) : -INFINITY;
   }
 }
 
@@ -426,7 +420,7 @@ int launch_partial_latent(const PartialArgs& a, hipStream_t stream, bool* handle
   *handled = true;
   const int n_tiles = (a.max_rows + kRows - 1) / kRows;
   const long long units = (long long)a.num_parts * a.Hkv;
-  const long long blocks = (units + 7) / 8 * 8 * n_tiles;
+  const long long blocks = units * n_tiles;
   if (blocks == 0) return PDK_OK;
   if (blocks > 0x7FFFFFFFLL) return fail(PDK_ERR_SHAPE, "grid too large (%lld)", blocks);
   hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(64 * kWaves), 0, stream, a);
