@@ -99,6 +99,29 @@ def time_steps(torch, parts, steps, warmup):
     return wall_ms, [timer.mean_us(sp) for sp in spans]
 
 
+def time_cold(torch, parts, steps, dev):
+    """Mean device time (us) of one step run after a 512 MiB device read
+    (a sum) that evicts the step's data from the 256 MB last-level (MALL)
+    cache, as the other layers of a model would between two decode steps of
+    one layer. The read is outside the timed span; HIP events bracket the
+    step's launches. A read, not a write: evicting dirty lines would charge
+    their write-back to the step."""
+    scratch = torch.zeros(128 << 20, dtype=torch.float32, device=dev)
+    for _ in range(2):
+        scratch.sum()
+    timer = Timer(torch)
+    spans = []
+    for _ in range(steps):
+        scratch.sum()
+        a = timer.mark()
+        for f in parts:
+            f()
+        spans.append((a, timer.mark()))
+    torch.cuda.synchronize()
+    del scratch
+    return timer.mean_us(spans)
+
+
 def cpu_baseline(batches, budget_s=15.0):
     """The f64 oracle, whole requests with all heads, on a bounded sample:
     GB of KV attended per second on one host thread."""
@@ -131,13 +154,14 @@ def planned(torch, pdk, b, params, dev):
 
 
 def run_plan_steps(args, torch, pdk, b, pool, q, plan, dev):
-    """Timed steps of a planned decode: (wall ms per step, partials us, merge us)."""
+    """Timed steps of a planned decode: (wall ms per step, partials us, merge
+    us, cold-cache us per step)."""
     out = torch.empty((b.batch, b.num_q_heads, b.head_dim_v), dtype=torch.float32, device=dev)
     lse = torch.empty((b.batch, b.num_q_heads), dtype=torch.float32, device=dev)
-    wall_ms, (t_part, t_merge) = time_steps(
-        torch, [lambda: plan.run_partials(pool, q, b.sm_scale), lambda: plan.run_merge(out, lse)],
-        args.steps, args.warmup)
-    return wall_ms, t_part, t_merge
+    parts = [lambda: plan.run_partials(pool, q, b.sm_scale), lambda: plan.run_merge(out, lse)]
+    wall_ms, (t_part, t_merge) = time_steps(torch, parts, args.steps, args.warmup)
+    cold_us = time_cold(torch, parts, args.steps, dev)
+    return wall_ms, t_part, t_merge, cold_us
 
 
 def bench_flat(args, torch, pdk, W, dev):
@@ -145,7 +169,7 @@ def bench_flat(args, torch, pdk, W, dev):
     pool, csr, q = device_batch(torch, pdk, b, dev)
     S = b.partition_tokens
     plan, plan_us = planned(torch, pdk, b, pdk.CascadeParams(enabled=0, l1_partition_tokens=S), dev)
-    wall_ms, t_part, t_merge = run_plan_steps(args, torch, pdk, b, pool, q, plan, dev)
+    wall_ms, t_part, t_merge, cold_us = run_plan_steps(args, torch, pdk, b, pool, q, plan, dev)
     stats, _ = plan.stats()
     R = stats["suffix_chunks"]
     Hq, Dv = b.num_q_heads, b.head_dim_v
@@ -177,6 +201,8 @@ def bench_flat(args, torch, pdk, W, dev):
                      "kernel": "partial_valu_kernel<bf16,bf16,D128,4 rows>",
                      "kernel_us": round(t_part, 2), "bytes_per_launch": alg},
         "kernels_us": {"partials": round(t_part, 2), "merge": round(t_merge, 2)},
+        "cold_cache": {"us_per_step": round(cold_us, 2),
+                       "unique_kv_GBps": round(kv / (cold_us * 1e-6) / 1e9, 2)},
     }
     batches = [b]
     if not args.no_cascade:
@@ -186,17 +212,32 @@ def bench_flat(args, torch, pdk, W, dev):
     return res
 
 
+def kernel_source_files(kernel_source):
+    """The kernel's translation unit and every local header it includes,
+    directly or through other local headers, in first-include order."""
+    import re
+    csrc = os.path.join(ROOT, "paged_split_kv_v2_amd", "csrc")
+    order, todo = [], [kernel_source]
+    while todo:
+        name = todo.pop(0)
+        path = os.path.join(csrc, name)
+        if name in order or not os.path.exists(path):
+            continue
+        order.append(name)
+        todo += re.findall(r'^#include "([^"]+)"', open(path).read(), re.M)
+    return order
+
+
 def kernel_source_sha(kernel_source):
-    """sha256 over the kernel's translation unit and the shared headers it
-    includes (device.h, internal.h), in that order."""
+    """sha256 over the kernel's translation unit and the local headers it
+    includes (kernel_source_files order)."""
     import hashlib
     csrc = os.path.join(ROOT, "paged_split_kv_v2_amd", "csrc")
+    if not os.path.exists(os.path.join(csrc, kernel_source)):
+        return None
     h = hashlib.sha256()
-    for name in (kernel_source, "device.h", "internal.h"):
-        path = os.path.join(csrc, name)
-        if not os.path.exists(path):
-            return None
-        h.update(open(path, "rb").read())
+    for name in kernel_source_files(kernel_source):
+        h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()
 
 
@@ -301,9 +342,12 @@ def bench_mla(args, torch, pdk, W, dev):
 
 def bench_cascade(args, torch, pdk, W, dev):
     """The shared-prefix workload alone: flat vs cascade arms; value = the
-    all-groups cascade's rate over unique KV bytes."""
+    all-groups cascade's rate over unique KV bytes. Dominant kernel: the
+    all-groups arm's partial launch (both levels in one grid)."""
     cv = bench_cascade_arms(args, torch, pdk, W, dev)
     best = cv["arms"]["cascade_all_groups"]
+    alg, part_us = cv["partial_launch_bytes"], best["partials_us"]
+    achieved = alg / (part_us * 1e-6) / 1e9
     return {"metric": METRIC, "value": best["unique_kv_GBps"], "unit": "GB/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": round(best["us_per_step"] / 1000, 5), "higher_is_better": True,
@@ -314,6 +358,15 @@ def bench_cascade(args, torch, pdk, W, dev):
                        "extra_tokens": 2048, "num_q_heads": 32, "num_kv_heads": 8,
                        "head_dim": 128, "page_size": 16},
             "us_per_step": best["us_per_step"], "frac_of_peak": best["frac_of_peak"],
+            "cold_cache": {"us_per_step": best["cold_cache_us_per_step"],
+                           "unique_kv_GBps": round(cv["unique_kv_bytes"] /
+                                                   (best["cold_cache_us_per_step"] * 1e-6) / 1e9, 2)},
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "traffic": traffic_record("partial_cascade.hip"),
+                         "kernel": "cascade_partial_kernel (level 0 + level 1 in one grid)",
+                         "kernel_us": part_us, "bytes_per_launch": alg},
+            "partial_state_bytes": cv["partial_state_bytes"],
             "cascade_vs_flat": cv}
 
 
@@ -331,10 +384,27 @@ def bench_copy(args, torch, pdk, W, dev):
             "config": {"workload": "copy_1GiB", "bytes_read": n, "bytes_written": n}}
 
 
+def cascade_partial_bytes(b, plan):
+    """Algorithmic HBM bytes of one cascade partial launch: every K/V byte of
+    both views once (the unique KV bytes), the query rows each level reads,
+    both views' page tables, and the partial states written; returns
+    (total, partial-state bytes)."""
+    members = len(plan.field("members"))
+    Hq, D = b.num_q_heads, b.head_dim_v
+    q_row = Hq * b.head_dim_k * b.q.itemsize
+    rows = int(plan.field("fused_merge_indptr")[-1])
+    tables = sum(plan.field(f).nbytes for f in ("l0_indptr", "l0_indices", "l0_len", "l1_indptr",
+                                                 "l1_indices", "l1_len", "group_indptr",
+                                                 "members"))
+    states = rows * Hq * (D + 1) * 4
+    return b.unique_kv_bytes() + (members + b.batch) * q_row + tables + states, states
+
+
 def bench_cascade_arms(args, torch, pdk, W, dev):
     """Shared-prefix workload (batch 72: 4 groups x 16 members sharing 4096
     tokens, private suffixes U[64,1024], 8 non-members of 2048 tokens): flat,
-    the page's single-subgroup cascade, and every qualifying group."""
+    the page's single-subgroup cascade, and every qualifying group (both
+    levels in one grid, and as two launches)."""
     b = W.cascade_shared_prefix()
     pool, csr, q = device_batch(torch, pdk, b, dev)
     kv = b.unique_kv_bytes()
@@ -345,19 +415,27 @@ def bench_cascade_arms(args, torch, pdk, W, dev):
                                                        l0_partition_tokens=512,
                                                        l1_partition_tokens=512)),
             ("cascade_all_groups", pdk.CascadeParams(enabled=1, max_groups=0,
-                                                     l0_partition_tokens=512,
-                                                     l1_partition_tokens=512))):
+                                                     l0_partition_tokens=1024,
+                                                     l1_partition_tokens=512)),
+            ("cascade_all_groups_two_launches",
+             pdk.CascadeParams(enabled=1, max_groups=0, l0_partition_tokens=256,
+                               l1_partition_tokens=512, fuse_levels=0))):
         plan, plan_us = planned(torch, pdk, b, params, dev)
-        wall_ms, t_part, t_merge = run_plan_steps(args, torch, pdk, b, pool, q, plan, dev)
+        wall_ms, t_part, t_merge, cold_us = run_plan_steps(args, torch, pdk, b, pool, q, plan,
+                                                           dev)
         stats, decline = plan.stats()
+        if name == "cascade_all_groups":
+            part_bytes, state_bytes = cascade_partial_bytes(b, plan)
         arms[name] = {"us_per_step": round(wall_ms * 1000, 2),
                       "partials_us": round(t_part, 2), "merge_us": round(t_merge, 2),
+                      "cold_cache_us_per_step": round(cold_us, 2),
                       "unique_kv_GBps": round(kv / (wall_ms * 1e-3) / 1e9, 2),
                       "frac_of_peak": round(kv / (wall_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                       "plan_host_us": round(plan_us, 1), "members": stats["members"],
                       "shared_pages": stats["shared_pages"], "decline": decline}
         del plan
     return {"workload": "cascade_shared_prefix_b72", "unique_kv_bytes": kv,
+            "partial_launch_bytes": part_bytes, "partial_state_bytes": state_bytes,
             "flat_read_bytes": b.read_kv_bytes(), "arms": arms,
             "speedup_all_groups": round(arms["flat"]["us_per_step"] /
                                         arms["cascade_all_groups"]["us_per_step"], 3),

@@ -207,6 +207,11 @@ typedef struct {
                                   0: every qualifying group; k: the best k */
   int32_t l0_partition_tokens; /* level-0 partition size, multiple of P */
   int32_t l1_partition_tokens; /* level-1 (and flat) partition size, multiple of P */
+  int32_t fuse_levels;         /* 1 (default): levels 0 and 1 in one grid when a
+                                  fused kernel covers the shape (bf16 pool and
+                                  queries, head dim 128, pages >= 16 tokens,
+                                  3-4 query heads per KV head), bit-identical
+                                  to two launches; 0: two launches */
 } pdk_cascade_params;
 
 void pdk_cascade_params_default(pdk_cascade_params* params);

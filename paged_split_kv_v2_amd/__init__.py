@@ -65,7 +65,8 @@ class _CSR(ctypes.Structure):
 class _Params(ctypes.Structure):
     _fields_ = [("enabled", ctypes.c_int32), ("min_shared_pages", ctypes.c_int32),
                 ("min_members", ctypes.c_int32), ("max_groups", ctypes.c_int32),
-                ("l0_partition_tokens", ctypes.c_int32), ("l1_partition_tokens", ctypes.c_int32)]
+                ("l0_partition_tokens", ctypes.c_int32), ("l1_partition_tokens", ctypes.c_int32),
+                ("fuse_levels", ctypes.c_int32)]
 
 
 _P, _I, _F, _S, _L = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t, ctypes.c_int64
@@ -341,10 +342,11 @@ class CascadeParams:
     max_groups: int = 1
     l0_partition_tokens: int = 256
     l1_partition_tokens: int = 512
+    fuse_levels: int = 1
 
     def struct(self) -> _Params:
         return _Params(self.enabled, self.min_shared_pages, self.min_members, self.max_groups,
-                       self.l0_partition_tokens, self.l1_partition_tokens)
+                       self.l0_partition_tokens, self.l1_partition_tokens, self.fuse_levels)
 
 
 class CascadePlan:

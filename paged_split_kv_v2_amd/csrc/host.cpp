@@ -92,11 +92,12 @@ static int check_query(const void* q, int q_dtype, int Hq, const pdk_kv_pool* po
   return PDK_OK;
 }
 
-int partial_rows(const pdk_kv_pool* pool, const pdk_csr* csr, const void* q, int q_dtype, int Hq,
+int partial_args(const pdk_kv_pool* pool, const pdk_csr* csr, const void* q, int q_dtype, int Hq,
                  float sm_scale, int S, const int* part_indptr, int num_parts,
                  const int* member_indptr, const int* members, int max_members, int G,
-                 const int* out_row_base, float* v_out, float* lse_out, hipStream_t stream,
-                 const int2* work) {
+                 const int* out_row_base, float* v_out, float* lse_out, const int2* work,
+                 PartialArgs* out, bool* empty) {
+  *empty = true;
   int st = check_pool(pool);
   if (st) return st;
   if ((st = check_query(q, q_dtype, Hq, pool))) return st;
@@ -133,6 +134,22 @@ int partial_rows(const pdk_kv_pool* pool, const pdk_csr* csr, const void* q, int
   a.v_out = v_out;
   a.lse_out = lse_out;
   a.work = work;
+  *out = a;
+  *empty = false;
+  return PDK_OK;
+}
+
+int partial_rows(const pdk_kv_pool* pool, const pdk_csr* csr, const void* q, int q_dtype, int Hq,
+                 float sm_scale, int S, const int* part_indptr, int num_parts,
+                 const int* member_indptr, const int* members, int max_members, int G,
+                 const int* out_row_base, float* v_out, float* lse_out, hipStream_t stream,
+                 const int2* work) {
+  PartialArgs a{};
+  bool empty = true;
+  int st = partial_args(pool, csr, q, q_dtype, Hq, sm_scale, S, part_indptr, num_parts,
+                        member_indptr, members, max_members, G, out_row_base, v_out, lse_out,
+                        work, &a, &empty);
+  if (st || empty) return st;
   return launch_partial(a, stream);
 }
 

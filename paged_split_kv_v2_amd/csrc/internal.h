@@ -66,6 +66,11 @@ int launch_partial_latent(const PartialArgs& a, hipStream_t stream, bool* handle
 // global->LDS loads, products on the matrix cores.
 int launch_partial_dma(const PartialArgs& a, hipStream_t stream, bool* handled);
 int valu_max_rows(int head_dim);
+// Level 0 (a0, stacked) and level 1 (a1, flat) of a cascade step in one
+// grid, when both fit the fused kernel's instantiations (*handled); the
+// partial rows equal those of two launch_partial calls.
+int launch_cascade_partials(const PartialArgs& a0, const PartialArgs& a1, hipStream_t stream,
+                            bool* handled);
 // out_stride: output row i is written at row i * out_stride of v_out / lse_out
 int launch_merge(const float* v_in, const float* lse_in, int num_in, const int* o_indptr,
                  int num_out, int H, int D, float* v_out, float* lse_out, int out_stride,
@@ -80,6 +85,13 @@ int partial_rows(const pdk_kv_pool* pool, const pdk_csr* view, const void* q, in
                  const int* member_indptr, const int* members, int max_members, int G,
                  const int* out_row_base, float* v_out, float* lse_out, hipStream_t stream,
                  const int2* work = nullptr);
+// The checks of partial_rows, filling *out instead of launching; *empty
+// when the view has nothing to compute.
+int partial_args(const pdk_kv_pool* pool, const pdk_csr* view, const void* q, int q_dtype, int Hq,
+                 float sm_scale, int S, const int* part_indptr, int num_parts,
+                 const int* member_indptr, const int* members, int max_members, int G,
+                 const int* out_row_base, float* v_out, float* lse_out, const int2* work,
+                 PartialArgs* out, bool* empty);
 int merge_rows(const float* v_in, const float* lse_in, int num_in, const int* o_indptr,
                int num_out, int H, int D, float* v_out, float* lse_out, int out_stride,
                hipStream_t stream);

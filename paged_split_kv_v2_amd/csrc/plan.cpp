@@ -118,6 +118,7 @@ void pdk_cascade_params_default(pdk_cascade_params* p) {
   p->max_groups = 1;
   p->l0_partition_tokens = 256;
   p->l1_partition_tokens = 512;
+  p->fuse_levels = 1;
 }
 
 int pdk_cascade_plan_create(const pdk_csr* csr, int32_t P, const pdk_cascade_params* params,
@@ -132,6 +133,8 @@ int pdk_cascade_plan_create(const pdk_csr* csr, int32_t P, const pdk_cascade_par
   if (pr.l0_partition_tokens <= 0 || pr.l0_partition_tokens % P ||
       pr.l1_partition_tokens <= 0 || pr.l1_partition_tokens % P)
     return fail(PDK_ERR_ARG, "partition sizes must be positive multiples of page_size %d", P);
+  if (pr.fuse_levels != 0 && pr.fuse_levels != 1)
+    return fail(PDK_ERR_ARG, "fuse_levels must be 0 or 1");
 
   const int B = csr->batch;
   const int32_t* indptr = csr->indptr;
@@ -362,20 +365,31 @@ int pdk_run_cascade_partials(const pdk_cascade_plan* plan, const pdk_kv_pool* po
 
   // level 0: each selected group's span once, members stacked KV-head-major,
   // partials written straight into the members' rows
+  PartialArgs a0{}, a1{};
+  bool empty0 = true, empty1 = true;
   if (plan->n_l0_parts > 0) {
     pdk_csr v0{base + o.l0_indptr, base + o.l0_indices, base + o.l0_len, plan->n_groups, 0};
-    int st = partial_rows(pool, &v0, q, q_dtype, Hq, sm_scale, plan->params.l0_partition_tokens,
+    int st = partial_args(pool, &v0, q, q_dtype, Hq, sm_scale, plan->params.l0_partition_tokens,
                           base + o.l0_parts, plan->n_l0_parts, base + o.group_indptr,
                           base + o.members, plan->max_members, G, base + o.member_rows, v_part,
-                          lse_part, stream, reinterpret_cast<const int2*>(base + o.l0_work));
+                          lse_part, reinterpret_cast<const int2*>(base + o.l0_work), &a0, &empty0);
     if (st) return st;
   }
   // level 1: every request's remaining range (the flat batch when declined)
   pdk_csr v1{base + o.l1_indptr, base + o.l1_indices, base + o.l1_len, plan->batch, 0};
-  return partial_rows(pool, &v1, q, q_dtype, Hq, sm_scale, plan->params.l1_partition_tokens,
-                      base + o.l1_parts, plan->n_l1_parts, nullptr, nullptr, 0, G,
-                      base + o.l1_rows, v_part, lse_part, stream,
-                      reinterpret_cast<const int2*>(base + o.l1_work));
+  int st = partial_args(pool, &v1, q, q_dtype, Hq, sm_scale, plan->params.l1_partition_tokens,
+                        base + o.l1_parts, plan->n_l1_parts, nullptr, nullptr, 0, G,
+                        base + o.l1_rows, v_part, lse_part,
+                        reinterpret_cast<const int2*>(base + o.l1_work), &a1, &empty1);
+  if (st) return st;
+  // the two levels write disjoint rows: one grid when a fused kernel fits
+  if (!empty0 && !empty1 && plan->params.fuse_levels) {
+    bool handled = false;
+    st = launch_cascade_partials(a0, a1, stream, &handled);
+    if (st || handled) return st;
+  }
+  if (!empty0 && (st = launch_partial(a0, stream))) return st;
+  return empty1 ? PDK_OK : launch_partial(a1, stream);
 }
 
 int pdk_run_cascade_merge(const pdk_cascade_plan* plan, int32_t Hq, int32_t Dv, float* out,

@@ -57,6 +57,33 @@ def test_cascade_workload_reduced(gpu, max_groups):
     assert lse_err(lse, fl.cpu().numpy()) <= 1e-5
 
 
+@pytest.mark.parametrize("case", ["reduced", "ragged"])
+def test_fused_levels_equal_two_launches(gpu, case):
+    """Levels 0 and 1 in one grid (bf16 pool, head dim 128, 4 query heads
+    per KV head: the fused kernel's shape) write the same partial rows as the
+    two launches, so the outputs agree bit for bit; both against the oracle."""
+    if case == "reduced":
+        b = W.cascade_shared_prefix(seed=2006, groups=3, members=6, prefix_tokens=1024,
+                                    suffix_max=300, extra=4, extra_tokens=500)
+        s0, s1 = 256, 512
+    else:  # one-token suffixes, short extras, partitions that end mid-step
+        b = W.cascade_shared_prefix(seed=2007, groups=2, members=5, prefix_tokens=528,
+                                    suffix_min=1, suffix_max=90, extra=3, extra_tokens=17)
+        s0, s1 = 64, 48
+    pool, csr, q = to_device(b)
+    res = {}
+    for fuse in (1, 0):
+        params = gpu.CascadeParams(enabled=1, max_groups=0, l0_partition_tokens=s0,
+                                   l1_partition_tokens=s1, fuse_levels=fuse)
+        out, lse, plan = cascade(gpu, b, params, pool, q)
+        assert plan.stats()[1] == "none" and plan.stats()[0]["members"] > 4
+        res[fuse] = (out, lse)
+    assert np.array_equal(res[1][0], res[0][0]) and np.array_equal(res[1][1], res[0][1])
+    ro, rl = oatt.decode_attention(b)
+    assert_close(res[1][0], ro, TOL["bf16"], "fused cascade out")
+    assert_lse(res[1][1], rl, "fused cascade lse")
+
+
 def test_declined_plan_runs_flat(gpu):
     b = W.llama3_8b_flat(seed=2005, batch=5, min_len=100, max_len=900)
     pool, csr, q = to_device(b)
@@ -181,9 +208,9 @@ def test_member_major_stacking_reads_the_wrong_kv_head(gpu):
 
 
 def test_plan_runs_repeat_and_cover_empty_requests(gpu):
-    """Planned runs merge inside the level-1 launch (last workgroup per
-    request and KV head); counters must return to zero so that repeated runs
-    agree bit for bit, and an empty request still gets (0, -inf)."""
+    """Repeated runs of one uploaded plan agree bit for bit (no state is
+    carried between runs), with and without sharing, and an empty request
+    still gets (0, -inf)."""
     lens = [300, 0, 530, 530, 17, 0, 530]
     b = W.random_batch(81, batch=len(lens), page_size=16, num_q_heads=32, num_kv_heads=8,
                        head_dim=128, kv_dtype="bf16", q_dtype="bf16", min_len=0, max_len=0,
