@@ -25,7 +25,7 @@ Seeds: the workload numbered ``i`` below draws from
 from __future__ import annotations
 
 import math
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 from typing import Optional
 
 import numpy as np
@@ -60,7 +60,8 @@ def _normal(rng: np.random.Generator, shape) -> np.ndarray:
 
 @dataclass
 class PagedBatch:
-    """One decode step's inputs: a query token per request plus a paged pool."""
+    """One decode step's inputs: the queries (q [B, Hq, Dk] for one token per
+    request, [B, T, Hq, Dk] for T tokens) plus a paged pool."""
 
     name: str
     page_size: int
@@ -338,6 +339,30 @@ def mla_decode_share(seed: int = 1005, batch: int = 32, heads: int = 128,
                                     pad_blocks=4, latent=True, poison=poison)
     suffix.q = prefix.q  # one query token per sequence, shared by both ranges
     return MlaShare(prefix=prefix, suffix=suffix, chunk_tokens=chunk_tokens)
+
+
+# --------------------------------------------------------------------------
+# Multi-token query steps
+# --------------------------------------------------------------------------
+
+def with_query_tokens(batch: PagedBatch, q_tokens: int, seed: int) -> PagedBatch:
+    """The same pool and page table with ``q_tokens`` query tokens per
+    request: q [B, T, Hq, Dk] drawn N(0,1) from ``seed`` and stored in the
+    batch's query dtype. The range of each request is taken to end with the
+    step's new tokens (how the oracle and the kernels read it)."""
+    rng = np.random.default_rng(seed)
+    q = _encode(_normal(rng, (batch.batch, q_tokens, batch.num_q_heads, batch.head_dim_k)),
+                batch.q_dtype)
+    meta = dict(batch.meta, q_tokens=q_tokens)
+    return replace(batch, name=f"{batch.name}_t{q_tokens}", q=q, meta=meta)
+
+
+def mla_share_with_query_tokens(share: MlaShare, q_tokens: int, seed: int) -> MlaShare:
+    """An MLA share whose step carries ``q_tokens`` query tokens per request
+    (shared by the cached prefix and the new-token suffix)."""
+    pre = with_query_tokens(share.prefix, q_tokens, seed)
+    suf = replace(share.suffix, q=pre.q, meta=dict(share.suffix.meta, q_tokens=q_tokens))
+    return MlaShare(prefix=pre, suffix=suf, chunk_tokens=share.chunk_tokens)
 
 
 # --------------------------------------------------------------------------
