@@ -1,6 +1,7 @@
 """Benchmark: paged split-KV decode on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload flat|cascade|merge|mla]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--workload flat|cascade|merge|mla|flat_mt|mla_mt|copy]
 
 A step is one attention layer's decode for the whole batch: every partial
 launch and every merge of the path. Inputs are seeded synthetic tensors
@@ -210,6 +211,97 @@ def bench_flat(args, torch, pdk, W, dev):
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(batches)
     return res
+
+
+def bench_flat_mt(args, torch, pdk, W, dev, T=4):
+    """The Llama-3-8B-shaped flat workload with a step of T = 4 query tokens
+    per request, causal over each range (a 4-token verification step):
+    partials of every (request, partition, token, head), then one merge per
+    request over the (token, head) pairs."""
+    b = W.with_query_tokens(W.llama3_8b_flat(), T, 1006)
+    pool, csr, q = device_batch(torch, pdk, b, dev)
+    S = b.partition_tokens
+    pind = pdk.partition_indptr(b.kv_len, S)
+    pind_d = torch.from_numpy(pind).to(dev)
+    R, B, Hq, Dv = int(pind[-1]), b.batch, b.num_q_heads, b.head_dim_v
+    v = torch.empty((R, T, Hq, Dv), dtype=torch.float32, device=dev)
+    l = torch.empty((R, T, Hq), dtype=torch.float32, device=dev)
+    out = torch.empty((B, T * Hq, Dv), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, T * Hq), dtype=torch.float32, device=dev)
+    parts = [lambda: pdk.paged_multi_token_partial(pool, csr, q, b.sm_scale, True, S, pind_d, R,
+                                                   v, l),
+             lambda: pdk.merge_states(v.view(R, T * Hq, Dv), l.view(R, T * Hq), pind_d, out, lse)]
+    wall_ms, (t_part, t_merge) = time_steps(torch, parts, args.steps, args.warmup)
+    cold_us = time_cold(torch, parts, args.steps, dev)
+    kv = b.unique_kv_bytes()
+    alg = (kv + b.q.nbytes + R * T * Hq * (Dv + 1) * 4 + b.indices.nbytes + b.kv_len.nbytes
+           + (B + 1) * 4)
+    value = kv / (wall_ms * 1e-3) / 1e9
+    achieved = alg / (t_part * 1e-6) / 1e9
+    return {"metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": f"llama3_8b_flat_{T}_token_causal_step", "batch": B,
+                       "query_tokens": T, "causal": True, "num_q_heads": Hq,
+                       "num_kv_heads": b.num_kv_heads, "head_dim": Dv,
+                       "page_size": b.page_size, "partition_tokens": S,
+                       "context_tokens": "uniform[1024,8192]",
+                       "total_tokens": int(b.kv_len.sum()), "partitions": R},
+            "us_per_step": round(wall_ms * 1000, 2),
+            "frac_of_peak": round(value / HBM_PEAK_GBS, 4),
+            "cold_cache": {"us_per_step": round(cold_us, 2),
+                           "unique_kv_GBps": round(kv / (cold_us * 1e-6) / 1e9, 2)},
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "traffic": None,
+                         "kernel": f"multi-token partial ({T * b.group} rows per KV head)",
+                         "kernel_us": round(t_part, 2), "bytes_per_launch": alg},
+            "kernels_us": {"partials": round(t_part, 2), "merge": round(t_merge, 2)}}
+
+
+def bench_mla_mt(args, torch, pdk, W, dev):
+    """The MLA decode share with a 4-token step: every token sees the whole
+    fp8 cached prefix (chunks non-causal) and the bf16 suffix causally."""
+    T = 4
+    share = W.mla_share_with_query_tokens(W.mla_decode_share(), T, 1007)
+    pre, suf = share.prefix, share.suffix
+    p_pool, _, q = device_batch(torch, pdk, pre, dev)
+    s_pool, _, _ = device_batch(torch, pdk, suf, dev)
+    plan = pdk.ChunkedPlan((pre.indptr, pre.indices, pre.kv_len), pre.page_size,
+                           share.chunk_tokens, pre.partition_tokens,
+                           (suf.indptr, suf.indices, suf.kv_len), suf.page_size,
+                           suf.partition_tokens)
+    Hq, Dv = pre.num_q_heads, pre.head_dim_v
+    plan.upload(T * Hq, Dv, dev)
+    out = torch.empty((pre.batch, T, Hq, Dv), dtype=torch.float32, device=dev)
+    lse = torch.empty((pre.batch, T, Hq), dtype=torch.float32, device=dev)
+    parts = [lambda: plan.run(p_pool, s_pool, q, pre.sm_scale, out, lse)]
+    wall_ms, (step_us,) = time_steps(torch, parts, args.steps, args.warmup)
+    cold_us = time_cold(torch, parts, args.steps, dev)
+    tok_pre, tok_suf = int(pre.kv_len.sum()), int(suf.kv_len.sum())
+    flop_tok = 2 * Hq * (pre.head_dim_k + Dv)
+    # causal suffix: token t of a request sees suffix_len - T + t + 1 positions
+    seen_suf = sum(T * int(n) - T * (T - 1) // 2 for n in suf.kv_len)
+    flops_step = flop_tok * (T * tok_pre + seen_suf)
+    kv_bytes = pre.unique_kv_bytes() + suf.unique_kv_bytes()
+    return {"metric": "MLA decode share: MFMA TFLOP/s (frac of bf16 peak) + µs/step",
+            "value": round(flops_step / (wall_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(wall_ms, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16 (fp8 e4m3 KV dequantized to bf16)",
+            "data": "synthetic",
+            "config": {"workload": "mla_decode_share_b32_ctx16384_fp8_4_token_step",
+                       "batch": pre.batch, "query_tokens": T, "num_q_heads": Hq,
+                       "head_dim_k": pre.head_dim_k, "head_dim_v": Dv,
+                       "page_size": pre.page_size, "chunk_tokens": share.chunk_tokens,
+                       "partition_tokens": pre.partition_tokens,
+                       "suffix_tokens": int(suf.kv_len[0])},
+            "us_per_step": round(wall_ms * 1000, 2), "step_device_us": round(step_us, 2),
+            "cold_cache": {"us_per_step": round(cold_us, 2)},
+            "kv_bytes": kv_bytes, "flops_per_step": flops_step,
+            "frac_of_mfma_peak": round(flops_step / (wall_ms * 1e-3) / 1e12 /
+                                       MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
 def kernel_source_files(kernel_source):
@@ -448,7 +540,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="flat", choices=["flat", "cascade", "merge", "mla", "copy"])
+    ap.add_argument("--workload", default="flat",
+                    choices=["flat", "cascade", "merge", "mla", "copy", "flat_mt", "mla_mt"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cascade", action="store_true")
     args = ap.parse_args()
@@ -464,7 +557,8 @@ def main():
         sys.exit(2)
     pdk.lib()
     res = {"flat": bench_flat, "cascade": bench_cascade, "merge": bench_merge, "mla": bench_mla,
-           "copy": bench_copy}[args.workload](args, torch, pdk, W, "cuda:0")
+           "copy": bench_copy, "flat_mt": bench_flat_mt,
+           "mla_mt": bench_mla_mt}[args.workload](args, torch, pdk, W, "cuda:0")
     print(json.dumps(res), flush=True)
 
 

@@ -173,6 +173,37 @@ int pdk_decode_flat(const pdk_kv_pool* pool, const pdk_csr* csr_dev, const void*
                     int32_t num_partitions, float* out, float* lse_out, void* workspace,
                     size_t workspace_bytes, hipStream_t stream);
 
+/* Multi-token steps: q_tokens = T >= 1 query tokens per request in one
+ * step (verification of speculated tokens, chunked prefill of a few tokens).
+ * q [batch, T, Hq, Dk] (f32|bf16); the request's range (kv_len tokens)
+ * already holds the step's T new tokens as its last T tokens. causal = 1:
+ * token t sees positions 0 .. kv_len[b] - T + t, its own and the earlier
+ * ones; a token that sees nothing of a partition gets the empty state
+ * (0, -inf) there. causal = 0: every token sees the whole range (a cached
+ * prefix, [DCP-PR, 3.2 figure]: cached chunks are attended non-causally).
+ * Outputs v_part [num_partitions, T, Hq, head_dim_v], lse_part
+ * [num_partitions, T, Hq]. T = 1 gives pdk_paged_decode_partial's results
+ * for either value of causal. Errors: as pdk_paged_decode_partial, plus
+ * PDK_ERR_ARG for T < 1 or causal outside {0, 1}. */
+int pdk_paged_multi_token_partial(const pdk_kv_pool* pool, const pdk_csr* csr_dev,
+                                  const void* q, int32_t q_dtype, int32_t num_q_heads,
+                                  int32_t q_tokens, int32_t causal, float sm_scale,
+                                  int32_t partition_tokens, const int32_t* part_indptr_dev,
+                                  int32_t num_partitions, float* v_part, float* lse_part,
+                                  hipStream_t stream);
+
+/* pdk_paged_multi_token_partial + pdk_merge_states over each request's
+ * partitions, the (token, head) pairs merged as T*Hq heads. out
+ * [batch, T, Hq, head_dim_v], lse_out [batch, T, Hq] (may be NULL).
+ * workspace: device, at least
+ * pdk_decode_flat_workspace_bytes(num_partitions, T * Hq, head_dim_v) bytes. */
+int pdk_multi_token_flat(const pdk_kv_pool* pool, const pdk_csr* csr_dev, const void* q,
+                         int32_t q_dtype, int32_t num_q_heads, int32_t q_tokens, int32_t causal,
+                         float sm_scale, int32_t partition_tokens,
+                         const int32_t* part_indptr_dev, int32_t num_partitions, float* out,
+                         float* lse_out, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
 /* Stack the query heads of M members KV-head-major, [M, Hkv, G, D] ->
  * [Hkv, M, G, D] [cascade-PR, "The decomposition"]: q0[h0] = q[members[m],
  * kv*G + g] for h0 = kv*(M*G) + m*G + g. q [*, Hkv*G, D] (f32|bf16),
@@ -326,6 +357,20 @@ int pdk_run_chunked_decode(const pdk_chunked_plan* plan, const pdk_kv_pool* pref
                            int32_t num_q_heads, float sm_scale, float* out, float* lse_out,
                            float* chunk_out, float* chunk_lse, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
+
+/* pdk_run_chunked_decode for a step of T = q_tokens query tokens per
+ * request, q [B, T, Hq, Dk]: the cached chunks non-causally (every token
+ * sees the whole cached prefix), the suffix causally (token t sees suffix
+ * positions 0 .. suffix_len - T + t), then the same merges with the
+ * (token, head) pairs as T*Hq heads. out [B, T, Hq, Dv], lse_out [B, T, Hq];
+ * chunk_out/chunk_lse (optional) [chunks, T, Hq, Dv] / [chunks, T, Hq].
+ * The workspace is pdk_chunked_workspace_bytes(plan, T * Hq, Dv) bytes,
+ * uploaded with pdk_chunked_plan_upload. T = 1 is pdk_run_chunked_decode. */
+int pdk_run_chunked_multi_token(const pdk_chunked_plan* plan, const pdk_kv_pool* prefix_pool,
+                                const pdk_kv_pool* suffix_pool, const void* q, int32_t q_dtype,
+                                int32_t num_q_heads, int32_t q_tokens, float sm_scale,
+                                float* out, float* lse_out, float* chunk_out, float* chunk_lse,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Thread-local description of the last non-OK status on this thread. */
 const char* pdk_last_error(void);

@@ -27,6 +27,7 @@ __all__ = [
     "PdkError", "lib", "KVPool", "DeviceCSR", "CascadeParams", "CascadePlan", "ChunkedPlan",
     "partition_indptr", "validate_csr", "parse_switch", "cascade_enabled_from_env",
     "stacked_head_map", "paged_decode_partial", "merge_states", "decode_flat",
+    "paged_multi_token_partial", "multi_token_flat",
     "stack_heads", "unstack_heads", "fp8_dequant_bf16",
     "F32", "BF16", "FP8_E4M3", "DECLINE_NAMES",
 ]
@@ -99,6 +100,12 @@ _SIGS = {
     "pdk_chunked_workspace_bytes": (_S, [_P, _I, _I]),
     "pdk_chunked_plan_upload": (_I, [_P, _P, _S, _P]),
     "pdk_run_chunked_decode": (_I, [_P, _P, _P, _P, _I, _I, _F, _P, _P, _P, _P, _P, _S, _P]),
+    "pdk_paged_multi_token_partial": (_I, [_P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _I, _P, _P,
+                                           _P]),
+    "pdk_multi_token_flat": (_I, [_P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _I, _P, _P, _P, _S,
+                                  _P]),
+    "pdk_run_chunked_multi_token": (_I, [_P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _P, _P, _P, _S,
+                                         _P]),
     "pdk_last_error": (ctypes.c_char_p, []),
 }
 
@@ -302,6 +309,49 @@ def decode_flat(pool: KVPool, csr: DeviceCSR, q: torch.Tensor, sm_scale: float,
     return out, lse_out
 
 
+def paged_multi_token_partial(pool: KVPool, csr: DeviceCSR, q: torch.Tensor, sm_scale: float,
+                              causal: bool, partition_tokens: int, part_indptr: torch.Tensor,
+                              num_partitions: int, v_part: Optional[torch.Tensor] = None,
+                              lse_part: Optional[torch.Tensor] = None, stream=None):
+    """q [B, T, Hq, Dk] -> v_part [R, T, Hq, Dv], lse_part [R, T, Hq]."""
+    T, Hq = int(q.shape[1]), int(q.shape[2])
+    if v_part is None:
+        v_part = torch.empty((num_partitions, T, Hq, pool.head_dim_v), dtype=torch.float32,
+                             device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((num_partitions, T, Hq), dtype=torch.float32, device=q.device)
+    ps, cs = pool.struct(), csr.struct()
+    _check(lib().pdk_paged_multi_token_partial(ctypes.byref(ps), ctypes.byref(cs), _ptr(q),
+                                               _dtype_code(q), Hq, T, int(bool(causal)),
+                                               float(sm_scale), int(partition_tokens),
+                                               _ptr(part_indptr), int(num_partitions),
+                                               _ptr(v_part), _ptr(lse_part), _stream(stream)))
+    return v_part, lse_part
+
+
+def multi_token_flat(pool: KVPool, csr: DeviceCSR, q: torch.Tensor, sm_scale: float,
+                     causal: bool, partition_tokens: int, part_indptr: torch.Tensor,
+                     num_partitions: int, out: Optional[torch.Tensor] = None,
+                     lse_out: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None, stream=None):
+    """q [B, T, Hq, Dk] -> out [B, T, Hq, Dv], lse_out [B, T, Hq]."""
+    B, T, Hq = int(q.shape[0]), int(q.shape[1]), int(q.shape[2])
+    need = int(lib().pdk_decode_flat_workspace_bytes(num_partitions, T * Hq, pool.head_dim_v))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, T, Hq, pool.head_dim_v), dtype=torch.float32, device=q.device)
+    if lse_out is None:
+        lse_out = torch.empty((B, T, Hq), dtype=torch.float32, device=q.device)
+    ps, cs = pool.struct(), csr.struct()
+    _check(lib().pdk_multi_token_flat(ctypes.byref(ps), ctypes.byref(cs), _ptr(q), _dtype_code(q),
+                                      Hq, T, int(bool(causal)), float(sm_scale),
+                                      int(partition_tokens), _ptr(part_indptr),
+                                      int(num_partitions), _ptr(out), _ptr(lse_out),
+                                      _ptr(workspace), int(workspace.numel()), _stream(stream)))
+    return out, lse_out
+
+
 def stack_heads(q: torch.Tensor, members: torch.Tensor, num_kv_heads: int, stream=None):
     M = int(members.numel())
     Hq, D = int(q.shape[1]), int(q.shape[2])
@@ -469,18 +519,29 @@ class ChunkedPlan:
 
     def run(self, prefix_pool: KVPool, suffix_pool: KVPool, q: torch.Tensor, sm_scale: float,
             out=None, lse_out=None, chunk_out=None, chunk_lse=None, stream=None):
-        B, Hq = int(q.shape[0]), int(q.shape[1])
+        """q [B, Hq, Dk] (one token per request) or [B, T, Hq, Dk] (a step of
+        T tokens: cached chunks non-causal, suffix causal)."""
+        B = int(q.shape[0])
+        T, Hq = (int(q.shape[1]), int(q.shape[2])) if q.dim() == 4 else (1, int(q.shape[1]))
         Dv = prefix_pool.head_dim_v
-        if self.workspace is None:
-            self.upload(Hq, Dv, q.device, stream)
+        need = int(lib().pdk_chunked_workspace_bytes(self._h, T * Hq, Dv))
+        if self.workspace is None or self.workspace.numel() < need:
+            self.upload(T * Hq, Dv, q.device, stream)
+        lead = (B, T, Hq) if q.dim() == 4 else (B, Hq)
         if out is None:
-            out = torch.empty((B, Hq, Dv), dtype=torch.float32, device=q.device)
+            out = torch.empty((*lead, Dv), dtype=torch.float32, device=q.device)
         if lse_out is None:
-            lse_out = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+            lse_out = torch.empty(lead, dtype=torch.float32, device=q.device)
         p1, p2 = prefix_pool.struct(), suffix_pool.struct()
-        _check(lib().pdk_run_chunked_decode(self._h, ctypes.byref(p1), ctypes.byref(p2), _ptr(q),
-                                            _dtype_code(q), Hq, float(sm_scale), _ptr(out),
-                                            _ptr(lse_out), _ptr(chunk_out), _ptr(chunk_lse),
-                                            _ptr(self.workspace), int(self.workspace.numel()),
-                                            _stream(stream)))
+        if q.dim() == 4:
+            _check(lib().pdk_run_chunked_multi_token(
+                self._h, ctypes.byref(p1), ctypes.byref(p2), _ptr(q), _dtype_code(q), Hq, T,
+                float(sm_scale), _ptr(out), _ptr(lse_out), _ptr(chunk_out), _ptr(chunk_lse),
+                _ptr(self.workspace), int(self.workspace.numel()), _stream(stream)))
+        else:
+            _check(lib().pdk_run_chunked_decode(self._h, ctypes.byref(p1), ctypes.byref(p2),
+                                                _ptr(q), _dtype_code(q), Hq, float(sm_scale),
+                                                _ptr(out), _ptr(lse_out), _ptr(chunk_out),
+                                                _ptr(chunk_lse), _ptr(self.workspace),
+                                                int(self.workspace.numel()), _stream(stream)))
         return out, lse_out

@@ -96,7 +96,7 @@ int partial_args(const pdk_kv_pool* pool, const pdk_csr* csr, const void* q, int
                  float sm_scale, int S, const int* part_indptr, int num_parts,
                  const int* member_indptr, const int* members, int max_members, int G,
                  const int* out_row_base, float* v_out, float* lse_out, const int2* work,
-                 PartialArgs* out, bool* empty) {
+                 PartialArgs* out, bool* empty, int q_tokens, int causal) {
   *empty = true;
   int st = check_pool(pool);
   if (st) return st;
@@ -112,6 +112,10 @@ int partial_args(const pdk_kv_pool* pool, const pdk_csr* csr, const void* q, int
     return fail(PDK_ERR_ARG, "NULL device array");
   if (member_indptr && (!members || max_members <= 0))
     return fail(PDK_ERR_ARG, "stacked view without members");
+  if (q_tokens < 1 || (causal != 0 && causal != 1))
+    return fail(PDK_ERR_ARG, "q_tokens %d must be >= 1 and causal 0 or 1", q_tokens);
+  if (causal && member_indptr)
+    return fail(PDK_ERR_UNSUPPORTED, "causal masking is for flat views only");
   if (!aligned16(q) || !aligned16(v_out)) return fail(PDK_ERR_ARG, "q/v_part must be 16-byte aligned");
   PartialArgs a{};
   fill_pool_args(pool, a);
@@ -129,7 +133,9 @@ int partial_args(const pdk_kv_pool* pool, const pdk_csr* csr, const void* q, int
   a.scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
   a.member_indptr = member_indptr;
   a.members = members;
-  a.max_rows = member_indptr ? max_members * G : G;
+  a.q_tokens = q_tokens;
+  a.causal = causal;
+  a.max_rows = (member_indptr ? max_members : 1) * q_tokens * G;
   a.out_row_base = out_row_base;
   a.v_out = v_out;
   a.lse_out = lse_out;
@@ -143,12 +149,12 @@ int partial_rows(const pdk_kv_pool* pool, const pdk_csr* csr, const void* q, int
                  float sm_scale, int S, const int* part_indptr, int num_parts,
                  const int* member_indptr, const int* members, int max_members, int G,
                  const int* out_row_base, float* v_out, float* lse_out, hipStream_t stream,
-                 const int2* work) {
+                 const int2* work, int q_tokens, int causal) {
   PartialArgs a{};
   bool empty = true;
   int st = partial_args(pool, csr, q, q_dtype, Hq, sm_scale, S, part_indptr, num_parts,
                         member_indptr, members, max_members, G, out_row_base, v_out, lse_out,
-                        work, &a, &empty);
+                        work, &a, &empty, q_tokens, causal);
   if (st || empty) return st;
   return launch_partial(a, stream);
 }
@@ -167,10 +173,11 @@ int merge_rows(const float* v_in, const float* lse_in, int num_in, const int* o_
                       stream);
 }
 
-// Kernel choice for one partial launch: the matrix-core path when a KV head
-// serves at least 16 bf16 query rows (stacked level 0, MLA); otherwise the
-// vector path, which keeps up to 16 query rows per KV head in registers and
-// tiles more rows over several workgroups.
+// Kernel choice for one partial launch: the matrix-core paths for bf16
+// queries when a KV head serves more than 4 query rows (head dim 128 with
+// bf16 K/V) or at least 64 (MLA latent rows), and for more than 16 rows on
+// small pages; otherwise the vector path, which keeps up to 16 query rows per
+// KV head in registers and tiles more rows over several workgroups.
 int launch_partial(const PartialArgs& a, hipStream_t stream) {
   bool handled = false;
   int st = launch_partial_latent(a, stream, &handled);
@@ -275,6 +282,43 @@ int pdk_paged_decode_partial(const pdk_kv_pool* pool, const pdk_csr* csr, const 
   if ((st = check_query(q, q_dtype, Hq, pool))) return st;
   return partial_rows(pool, csr, q, q_dtype, Hq, sm_scale, S, part_indptr, num_parts, nullptr,
                       nullptr, 0, Hq / pool->num_kv_heads, part_indptr, v_part, lse_part, stream);
+}
+
+int pdk_paged_multi_token_partial(const pdk_kv_pool* pool, const pdk_csr* csr, const void* q,
+                                  int32_t q_dtype, int32_t Hq, int32_t T, int32_t causal,
+                                  float sm_scale, int32_t S, const int32_t* part_indptr,
+                                  int32_t num_parts, float* v_part, float* lse_part,
+                                  hipStream_t stream) {
+  int st = check_pool(pool);
+  if (st) return st;
+  if ((st = check_query(q, q_dtype, Hq, pool))) return st;
+  return partial_rows(pool, csr, q, q_dtype, Hq, sm_scale, S, part_indptr, num_parts, nullptr,
+                      nullptr, 0, Hq / pool->num_kv_heads, part_indptr, v_part, lse_part, stream,
+                      nullptr, T, causal);
+}
+
+int pdk_multi_token_flat(const pdk_kv_pool* pool, const pdk_csr* csr, const void* q,
+                         int32_t q_dtype, int32_t Hq, int32_t T, int32_t causal, float sm_scale,
+                         int32_t S, const int32_t* part_indptr, int32_t num_parts, float* out,
+                         float* lse_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_pool(pool);
+  if (st) return st;
+  if (!csr || !out) return fail(PDK_ERR_ARG, "NULL csr/out");
+  if (T < 1 || Hq <= 0 || (long long)T * Hq > 0x7FFFFFFF)
+    return fail(PDK_ERR_ARG, "q_tokens %d, num_q_heads %d", T, Hq);
+  const int H = T * Hq;  // (token, head) pairs merge as heads
+  const size_t need = pdk_decode_flat_workspace_bytes(num_parts, H, pool->head_dim_v);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(PDK_ERR_WORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
+  float* v_part = (float*)ws;
+  float* lse_part = (float*)((char*)ws + (((size_t)num_parts * H * pool->head_dim_v * 4 + 255) & ~(size_t)255));
+  if (num_parts > 0) {
+    st = pdk_paged_multi_token_partial(pool, csr, q, q_dtype, Hq, T, causal, sm_scale, S,
+                                       part_indptr, num_parts, v_part, lse_part, stream);
+    if (st) return st;
+  }
+  return pdk_merge_states(v_part, lse_part, num_parts, part_indptr, csr->batch, H,
+                          pool->head_dim_v, out, lse_out, stream);
 }
 
 int pdk_merge_states(const float* v_in, const float* lse_in, int32_t num_in,

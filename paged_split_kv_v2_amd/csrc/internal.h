@@ -43,6 +43,10 @@ struct PartialArgs {
   int Hq;
   int G;                      // query heads per KV head of the batch layout
   float scale_log2;           // sm_scale * log2(e)
+  // multi-token steps (flat views only): q is [B, T, Hq, Dk], states are
+  // [rows, T, Hq, Dv]; causal: token t sees positions <= kv_len - T + t
+  int q_tokens;               // T >= 1
+  int causal;
   // stacking; member_indptr == nullptr for a flat view
   const int* member_indptr;   // [batch+1] members of view request k
   const int* members;         // batch index of each member slot
@@ -80,18 +84,20 @@ int launch_merge(const float* v_in, const float* lse_in, int num_in, const int* 
 // pdk_paged_decode_partial / pdk_merge_states, plus stacking and row maps).
 // work: optional longest-first (view request, partition) items, one per
 // partition of the view, that replace the part_indptr order.
+// q_tokens / causal: multi-token steps (q [*, T, Hq, Dk], states
+// [*, T, Hq, Dv]); causal masking only on flat views.
 int partial_rows(const pdk_kv_pool* pool, const pdk_csr* view, const void* q, int q_dtype, int Hq,
                  float sm_scale, int S, const int* part_indptr, int num_parts,
                  const int* member_indptr, const int* members, int max_members, int G,
                  const int* out_row_base, float* v_out, float* lse_out, hipStream_t stream,
-                 const int2* work = nullptr);
+                 const int2* work = nullptr, int q_tokens = 1, int causal = 0);
 // The checks of partial_rows, filling *out instead of launching; *empty
 // when the view has nothing to compute.
 int partial_args(const pdk_kv_pool* pool, const pdk_csr* view, const void* q, int q_dtype, int Hq,
                  float sm_scale, int S, const int* part_indptr, int num_parts,
                  const int* member_indptr, const int* members, int max_members, int G,
                  const int* out_row_base, float* v_out, float* lse_out, const int2* work,
-                 PartialArgs* out, bool* empty);
+                 PartialArgs* out, bool* empty, int q_tokens = 1, int causal = 0);
 int merge_rows(const float* v_in, const float* lse_in, int num_in, const int* o_indptr,
                int num_out, int H, int D, float* v_out, float* lse_out, int out_stride,
                hipStream_t stream);

@@ -19,15 +19,18 @@ typedef void (*DmaFn)(const PartialArgs);
 }  // namespace
 
 // bf16 K/V pools of head dim 128 (separate K and V), bf16 queries, pages of
-// a power of two >= 4 tokens, more than 16 query rows per KV head (stacked
-// level-0 rows): this path takes the launch (*handled) with 4 waves (64
-// rows per row tile). With a few rows per KV head the vector kernel streams
-// faster: one wave per (partition, KV head) leaves room for only five waves
-// of two-stage rings per CU.
+// a power of two >= 4 tokens, more than 4 query rows per KV head (stacked
+// level-0 rows, multi-token steps, query groups of 8 or 16): this path takes
+// the launch (*handled) with 4 waves (64 rows per row tile). With up to 4
+// rows per KV head the vector kernel streams faster (three workgroups of 64
+// KB in flight per CU, against two of 48 KB here); from 8 rows on it spends
+// more on its register-held products than the LDS ring loses (measured on a
+// 64-request step of 8 and 16 rows per KV head: 277 and 283 us here against
+// 357 and 1046 us on the vector kernel).
 int launch_partial_dma(const PartialArgs& a, hipStream_t stream, bool* handled) {
   *handled = false;
   if (a.q_dtype != PDK_BF16 || a.kv_dtype != PDK_BF16 || a.v == nullptr || a.Dk != 128 ||
-      a.Dv != 128 || a.p_shift < 2 || a.max_rows <= 16)
+      a.Dv != 128 || a.p_shift < 2 || a.max_rows <= 4)
     return PDK_OK;
   const int nw = 4;
   DmaFn fn = partial_dma_kernel<128, 32, 4, 4, true>;

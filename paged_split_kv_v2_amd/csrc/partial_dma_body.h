@@ -32,6 +32,7 @@
 
 #include "device.h"
 #include "internal.h"
+#include "rows.h"
 
 namespace pdk {
 
@@ -109,7 +110,7 @@ __device__ __forceinline__ void partial_dma_body(const PartialArgs& a, const int
   }
   const bool stacked = a.member_indptr != nullptr;
   const int mbase = stacked ? a.member_indptr[b] : 0;
-  const int nrows = (stacked ? (a.member_indptr[b + 1] - mbase) : 1) * a.G;
+  const int nrows = view_rows(a, stacked, mbase, b);
   const int row0 = rt * 16 * NW;
   if (row0 >= nrows) return;  // uniform
 
@@ -118,6 +119,10 @@ __device__ __forceinline__ void partial_dma_body(const PartialArgs& a, const int
   const int start = p * a.S;
   int end = min(start + a.S, a.kv_len[b]);
   end = min(end, npages * a.P);
+  // causal rows: the tile loop stops at the last owned row's end; every
+  // owned row sees at least the positions below end_lo (uniform)
+  const int end_lo = min(end, visible_end(a, b, row0 / a.G));
+  end = min(end, visible_end(a, b, (min(row0 + 16 * NW, nrows) - 1) / a.G));
   const int shift = a.p_shift;
   const int pmask = a.P - 1;
   const int pg_first = start >> shift;
@@ -138,12 +143,14 @@ __device__ __forceinline__ void partial_dma_body(const PartialArgs& a, const int
   // the wave's 16 query rows as B fragments: lane -> row r16, dims 32ks + 8q4 + i
   u32x4_t qf[KS];
   const int my_row = row0 + 16 * wave + r16;
+  // positions this lane's row sees within the partition
+  const int my_end = min(end, visible_end(a, b, min(my_row, nrows - 1) / a.G));
   {
     int qb = b, head = 0;
     const bool live = my_row < nrows;
     if (live) {
       const int m = my_row / a.G, g = my_row % a.G;
-      qb = stacked ? a.members[mbase + m] : b;
+      qb = query_row(a, stacked, mbase, b, m);
       head = h * a.G + g;
     }
     // padding rows read row 0 of request qb: always a valid address
@@ -235,7 +242,7 @@ __device__ __forceinline__ void partial_dma_body(const PartialArgs& a, const int
 
     // row max over the lane groups (scaled log2 units)
     float cs = a.scale_log2, mx;
-    if (t0 + TT <= end) {
+    if (t0 + TT <= end_lo) {
       float hi = -INFINITY, lo = INFINITY;
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb)
@@ -252,7 +259,7 @@ __device__ __forceinline__ void partial_dma_body(const PartialArgs& a, const int
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int t = t0 + 16 * tb + 4 * q4 + jj;
-          s[tb][jj] = (t < end) ? s[tb][jj] * cs : -INFINITY;
+          s[tb][jj] = (t < my_end) ? s[tb][jj] * cs : -INFINITY;
           mx = fmaxf(mx, s[tb][jj]);
         }
       cs = 1.f;
@@ -329,8 +336,7 @@ __device__ __forceinline__ void partial_dma_body(const PartialArgs& a, const int
   l += __shfl_xor(l, 32);
   if (my_row < nrows) {
     const int m = my_row / a.G, g = my_row % a.G;
-    const int orow = (stacked ? a.out_row_base[mbase + m] : a.out_row_base[b]) + p;
-    const size_t o = (size_t)orow * a.Hq + h * a.G + g;
+    const size_t o = state_index(a, stacked, mbase, b, p, m, h * a.G + g);
     float* dst = a.v_out + o * D + 4 * q4;
     const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll

@@ -36,6 +36,7 @@
 
 #include "device.h"
 #include "internal.h"
+#include "rows.h"
 
 namespace pdk {
 
@@ -96,7 +97,7 @@ void partial_latent_kernel(const PartialArgs a) {
   __shared__ int sm_pid[kMaxPagesL];
 
   // block -> (unit = partition * Hkv + kv head, row tile): the row tiles of a
-  // unit are 8 blocks apart, 8 units per group
+  // unit are adjacent blocks
   const int n_tiles = (a.max_rows + kRows - 1) / kRows;
   const int bid = blockIdx.x;
   const int unit = bid / n_tiles;
@@ -121,7 +122,7 @@ void partial_latent_kernel(const PartialArgs a) {
   }
   const bool stacked = a.member_indptr != nullptr;
   const int mbase = stacked ? a.member_indptr[b] : 0;
-  const int nrows = (stacked ? (a.member_indptr[b + 1] - mbase) : 1) * a.G;
+  const int nrows = view_rows(a, stacked, mbase, b);
   const int row0 = tile * kRows;
   if (row0 >= nrows) return;  // uniform
 
@@ -130,6 +131,10 @@ void partial_latent_kernel(const PartialArgs a) {
   const int start = p * a.S;
   int end = min(start + a.S, a.kv_len[b]);
   end = min(end, npages * a.P);
+  // causal rows: the tile loop stops at the last owned row's end; every
+  // owned row sees at least the positions below end_lo (uniform)
+  const int end_lo = min(end, visible_end(a, b, row0 / a.G));
+  end = min(end, visible_end(a, b, (min(row0 + kRows, nrows) - 1) / a.G));
   const int shift = a.p_shift;
   const int pmask = a.P - 1;
   const int pg_first = start >> shift;
@@ -151,12 +156,14 @@ void partial_latent_kernel(const PartialArgs a) {
   // lane -> row r16, dims 32ks + 8q4 + i
   u32x4_t qf[KS];
   const int my_row = row0 + 16 * wave + r16;
+  // positions this lane's row sees within the partition
+  const int my_end = min(end, visible_end(a, b, min(my_row, nrows - 1) / a.G));
   {
     int qb = b, head = 0;
     const bool live = my_row < nrows;
     if (live) {
       const int m = my_row / a.G, g = my_row % a.G;
-      qb = stacked ? a.members[mbase + m] : b;
+      qb = query_row(a, stacked, mbase, b, m);
       head = h * a.G + g;
     }
     // row 0 of request qb stands in for padding rows: always a valid address
@@ -291,7 +298,7 @@ void partial_latent_kernel(const PartialArgs a) {
     // row max over the four lane groups, in scaled log2 units; a full tile
     // scales inside the exponent below, the last tile masks first
     float cs = a.scale_log2, mx;
-    if (t0 + kTT <= end) {
+    if (t0 + kTT <= end_lo) {
       float hi = fmaxf(s[0][0], s[1][0]), lo = fminf(s[0][0], s[1][0]);
 #pragma unroll
       for (int j = 1; j < 4; ++j) {
@@ -306,7 +313,7 @@ void partial_latent_kernel(const PartialArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int t = t0 + 16 * tb + 4 * q4 + j;
-          s[tb][j] = (t < end) ? s[tb][j] * cs : -INFINITY;
+          s[tb][j] = (t < my_end) ? s[tb][j] * cs : -INFINITY;
           mx = fmaxf(mx, s[tb][j]);
         }
       cs = 1.f;
@@ -385,8 +392,7 @@ void partial_latent_kernel(const PartialArgs a) {
   l += __shfl_xor(l, 32);
   if (my_row < nrows) {
     const int m = my_row / a.G, g = my_row % a.G;
-    const int orow = (stacked ? a.out_row_base[mbase + m] : a.out_row_base[b]) + p;
-    const size_t o = (size_t)orow * a.Hq + h * a.G + g;
+    const size_t o = state_index(a, stacked, mbase, b, p, m, h * a.G + g);
     float* dst = a.v_out + o * DV + 4 * q4;
     const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll

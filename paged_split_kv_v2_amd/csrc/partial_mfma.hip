@@ -39,6 +39,7 @@
 
 #include "device.h"
 #include "internal.h"
+#include "rows.h"
 
 namespace pdk {
 
@@ -114,7 +115,7 @@ __global__ __launch_bounds__(64 * NW) void partial_mfma_kernel(const PartialArgs
   }
   const bool stacked = a.member_indptr != nullptr;
   const int mbase = stacked ? a.member_indptr[b] : 0;
-  const int nrows = (stacked ? (a.member_indptr[b + 1] - mbase) : 1) * a.G;
+  const int nrows = view_rows(a, stacked, mbase, b);
   const int row0 = tile * 16 * NW;
   if (row0 >= nrows) return;  // uniform
 
@@ -123,6 +124,8 @@ __global__ __launch_bounds__(64 * NW) void partial_mfma_kernel(const PartialArgs
   const int start = p * a.S;
   int end = min(start + a.S, a.kv_len[b]);
   end = min(end, npages * a.P);
+  // causal rows: the tile loop stops at the last owned row's end
+  end = min(end, visible_end(a, b, (min(row0 + 16 * NW, nrows) - 1) / a.G));
   const int shift = a.p_shift;
   const int pmask = a.P - 1;
   const int pg_first = start >> shift;
@@ -143,12 +146,14 @@ __global__ __launch_bounds__(64 * NW) void partial_mfma_kernel(const PartialArgs
   // the wave's 16 query rows as MFMA B fragments (bf16)
   u32x4_t qf[KSTEPS];
   const int my_row = row0 + 16 * wave + r16;
+  // positions this lane's row sees within the partition
+  const int my_end = min(end, visible_end(a, b, min(my_row, nrows - 1) / a.G));
   {
     int qb = b, head = 0;
     const bool live = my_row < nrows;
     if (live) {
       const int m = my_row / a.G, g = my_row % a.G;
-      qb = stacked ? a.members[mbase + m] : b;
+      qb = query_row(a, stacked, mbase, b, m);
       head = h * a.G + g;
     }
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)qb * a.Hq + head) * DK;
@@ -311,7 +316,7 @@ __global__ __launch_bounds__(64 * NW) void partial_mfma_kernel(const PartialArgs
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int t = t0 + 16 * tb + 4 * q4 + j;
-        s[tb][j] = (t < end) ? s[tb][j] * a.scale_log2 : -INFINITY;
+        s[tb][j] = (t < my_end) ? s[tb][j] * a.scale_log2 : -INFINITY;
         mx = fmaxf(mx, s[tb][j]);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -374,8 +379,7 @@ __global__ __launch_bounds__(64 * NW) void partial_mfma_kernel(const PartialArgs
   l += __shfl_xor(l, 32);
   if (my_row < nrows) {
     const int m = my_row / a.G, g = my_row % a.G;
-    const int orow = (stacked ? a.out_row_base[mbase + m] : a.out_row_base[b]) + p;
-    const size_t o = (size_t)orow * a.Hq + h * a.G + g;
+    const size_t o = state_index(a, stacked, mbase, b, p, m, h * a.G + g);
     float* dst = a.v_out + o * DV + 4 * q4;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {

@@ -8,32 +8,38 @@ namespace pdk {
 
 namespace {
 
-template <int KT, int QT, int D, int GM, bool UNIF>
+template <int KT, int QT, int D, int GM, bool UNIF, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void partial_valu_kernel(const PartialArgs a) {
-  partial_valu_body<KT, QT, D, GM, UNIF>(a, blockIdx.x);
+  partial_valu_body<KT, QT, D, GM, UNIF, CAUSAL>(a, blockIdx.x);
 }
 
 typedef void (*KernelFn)(const PartialArgs);
 
-template <int KT, int QT, int D, bool U>
+template <int KT, int QT, int D, bool U, bool C>
 KernelFn pick_gm(int gm) {
   constexpr int E = D / 16;
   switch (gm) {
-    case 1: return partial_valu_kernel<KT, QT, D, 1, U>;
-    case 2: return partial_valu_kernel<KT, QT, D, 2, U>;
-    case 4: return partial_valu_kernel<KT, QT, D, 4, U>;
-    case 8: if constexpr (8 * E <= 128) return partial_valu_kernel<KT, QT, D, 8, U>; else return nullptr;
-    case 16: if constexpr (16 * E <= 128) return partial_valu_kernel<KT, QT, D, 16, U>; else return nullptr;
+    case 1: return partial_valu_kernel<KT, QT, D, 1, U, C>;
+    case 2: return partial_valu_kernel<KT, QT, D, 2, U, C>;
+    case 4: return partial_valu_kernel<KT, QT, D, 4, U, C>;
+    case 8: if constexpr (8 * E <= 128) return partial_valu_kernel<KT, QT, D, 8, U, C>; else return nullptr;
+    case 16: if constexpr (16 * E <= 128) return partial_valu_kernel<KT, QT, D, 16, U, C>; else return nullptr;
   }
   return nullptr;
 }
 
+template <int KT, int QT, int D>
+KernelFn pick_uc(int gm, bool unif, bool causal) {
+  if (causal) return unif ? pick_gm<KT, QT, D, true, true>(gm) : pick_gm<KT, QT, D, false, true>(gm);
+  return unif ? pick_gm<KT, QT, D, true, false>(gm) : pick_gm<KT, QT, D, false, false>(gm);
+}
+
 template <int KT, int QT>
-KernelFn pick_d(int d, int gm, bool unif) {
+KernelFn pick_d(int d, int gm, bool unif, bool causal) {
   switch (d) {
-    case 64: return unif ? pick_gm<KT, QT, 64, true>(gm) : pick_gm<KT, QT, 64, false>(gm);
-    case 128: return unif ? pick_gm<KT, QT, 128, true>(gm) : pick_gm<KT, QT, 128, false>(gm);
-    case 256: return unif ? pick_gm<KT, QT, 256, true>(gm) : pick_gm<KT, QT, 256, false>(gm);
+    case 64: return pick_uc<KT, QT, 64>(gm, unif, causal);
+    case 128: return pick_uc<KT, QT, 128>(gm, unif, causal);
+    case 256: return pick_uc<KT, QT, 256>(gm, unif, causal);
   }
   return nullptr;
 }
@@ -57,10 +63,12 @@ int launch_partial_valu(const PartialArgs& a, hipStream_t stream) {
   KernelFn fn = nullptr;
   const int kt = a.kv_dtype, qt = a.q_dtype;
   const bool unif = a.P >= 16;  // a wave's four tokens of one step share a page
-  if (kt == PDK_F32 && qt == PDK_F32) fn = pick_d<KV_F32, PDK_F32>(a.Dk, gm, unif);
-  else if (kt == PDK_F32 && qt == PDK_BF16) fn = pick_d<KV_F32, PDK_BF16>(a.Dk, gm, unif);
-  else if (kt == PDK_BF16 && qt == PDK_F32) fn = pick_d<KV_BF16, PDK_F32>(a.Dk, gm, unif);
-  else if (kt == PDK_BF16 && qt == PDK_BF16) fn = pick_d<KV_BF16, PDK_BF16>(a.Dk, gm, unif);
+  // one token per request sees its whole range: the causal mask is a no-op
+  const bool causal = a.causal && a.q_tokens > 1;
+  if (kt == PDK_F32 && qt == PDK_F32) fn = pick_d<KV_F32, PDK_F32>(a.Dk, gm, unif, causal);
+  else if (kt == PDK_F32 && qt == PDK_BF16) fn = pick_d<KV_F32, PDK_BF16>(a.Dk, gm, unif, causal);
+  else if (kt == PDK_BF16 && qt == PDK_F32) fn = pick_d<KV_BF16, PDK_F32>(a.Dk, gm, unif, causal);
+  else if (kt == PDK_BF16 && qt == PDK_BF16) fn = pick_d<KV_BF16, PDK_BF16>(a.Dk, gm, unif, causal);
   if (!fn)
     return fail(PDK_ERR_UNSUPPORTED,
                 "no vector kernel for kv dtype %d, q dtype %d, head dim %d, %d rows", kt, qt,

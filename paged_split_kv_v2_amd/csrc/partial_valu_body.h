@@ -39,6 +39,7 @@
 
 #include "device.h"
 #include "internal.h"
+#include "rows.h"
 
 namespace pdk {
 
@@ -96,11 +97,12 @@ struct Tile {
   uint32_t kw[T][NU];
   uint32_t vw[T][NU];
   bool valid[T];
+  int tok[T];  // position of each token (read only with causal rows)
 };
 
 // The work of one workgroup of 256 threads: `block` is its index in the
 // grid of its launch (the decomposition below is over that index).
-template <int KT, int QT, int D, int GM, bool UNIF>
+template <int KT, int QT, int D, int GM, bool UNIF, bool CAUSAL>
 __device__ __forceinline__ void partial_valu_body(const PartialArgs& a, const int block) {
   constexpr int E = D / 16;                          // elements per lane
   constexpr int NU = E * (KT == KV_F32 ? 4 : 2) / 4; // 32-bit words per lane per row
@@ -143,7 +145,7 @@ __device__ __forceinline__ void partial_valu_body(const PartialArgs& a, const in
 
   const bool stacked = a.member_indptr != nullptr;
   const int mbase = stacked ? a.member_indptr[b] : 0;
-  const int nrows = (stacked ? (a.member_indptr[b + 1] - mbase) : 1) * a.G;
+  const int nrows = view_rows(a, stacked, mbase, b);
   const int row0 = tile * GM;
   if (row0 >= nrows) return;  // uniform over the workgroup
 
@@ -152,6 +154,15 @@ __device__ __forceinline__ void partial_valu_body(const PartialArgs& a, const in
   const int start = p * a.S;
   int end = min(start + a.S, a.kv_len[b]);
   end = min(end, npages * a.P);
+  // causal rows: positions past the last owned row's end are never read
+  int lim[GM];
+#pragma unroll
+  for (int gi = 0; gi < GM; ++gi) lim[gi] = INT_MAX;
+  if constexpr (CAUSAL) {
+#pragma unroll
+    for (int gi = 0; gi < GM; ++gi) lim[gi] = visible_end(a, b, (row0 + gi) / a.G);
+    end = min(end, visible_end(a, b, (min(row0 + GM, nrows) - 1) / a.G));
+  }
   const int shift = a.p_shift;  // page size is a power of two on this path
 
   const int rg = tid >> 4;
@@ -176,7 +187,7 @@ __device__ __forceinline__ void partial_valu_body(const PartialArgs& a, const in
     for (int i = 0; i < QW; ++i) qw[gi][i] = 0;
     if (row < nrows) {
       const int m = row / a.G, g = row % a.G;
-      const int qb = stacked ? a.members[mbase + m] : b;
+      const int qb = query_row(a, stacked, mbase, b, m);
       const size_t qoff = ((size_t)qb * a.Hq + h * a.G + g) * a.Dk + j * E;
       if constexpr (QT == PDK_F32) {
         const float* qp = reinterpret_cast<const float*>(a.q) + qoff;
@@ -228,6 +239,7 @@ __device__ __forceinline__ void partial_valu_body(const PartialArgs& a, const in
       // in one page: its row base is wave-uniform (scalar address)
       if constexpr (UNIF) pid = __builtin_amdgcn_readfirstlane(pid);
       X.valid[u] = (t < end) && (pid >= 0);
+      X.tok[u] = t;
       pid = max(pid, 0);
       const uint32_t slot = (uint32_t)(tc & pmask);
       const char* kp = kbase + pid * kb_stride;
@@ -265,7 +277,8 @@ __device__ __forceinline__ void partial_valu_body(const PartialArgs& a, const in
     for (int u = 0; u < T; ++u)
 #pragma unroll
       for (int gi = 0; gi < GM; ++gi)
-        s[u * GM + gi] = X.valid[u] ? s[u * GM + gi] * a.scale_log2 : -INFINITY;
+        s[u * GM + gi] = (X.valid[u] && (!CAUSAL || X.tok[u] < lim[gi]))
+                             ? s[u * GM + gi] * a.scale_log2 : -INFINITY;
 
     // raise the reference maxima only where a score jumped past them
     float mx[GM];
@@ -388,8 +401,7 @@ __device__ __forceinline__ void partial_valu_body(const PartialArgs& a, const in
       num = fmaf(ww, sm_acc[w][gi][d], num);
     }
     const int m = row / a.G, g = row % a.G;
-    const int orow = (stacked ? a.out_row_base[mbase + m] : a.out_row_base[b]) + p;
-    const size_t o = (size_t)orow * a.Hq + h * a.G + g;
+    const size_t o = state_index(a, stacked, mbase, b, p, m, h * a.G + g);
     a.v_out[o * a.Dv + d] = (L > 0.f) ? num / L : 0.f;
     if (d == 0) a.lse_out[o] = (L > 0.f) ? M + log2f(L) : -INFINITY;
   }

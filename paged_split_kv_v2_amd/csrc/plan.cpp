@@ -562,12 +562,20 @@ int pdk_chunked_plan_upload(pdk_chunked_plan* plan, void* ws, size_t ws_bytes, h
   return PDK_OK;
 }
 
-int pdk_run_chunked_decode(const pdk_chunked_plan* plan, const pdk_kv_pool* pre_pool,
-                           const pdk_kv_pool* suf_pool, const void* q, int32_t q_dtype,
-                           int32_t Hq, float sm_scale, float* out, float* lse_out,
-                           float* chunk_out, float* chunk_lse, void* ws, size_t ws_bytes,
-                           hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The chunked split for a step of T query tokens per request: the cached
+// chunks non-causally, the suffix causally (T = 1: plain decode); the merges
+// take the (token, head) pairs as H = T*Hq heads.
+int run_chunked(const pdk_chunked_plan* plan, const pdk_kv_pool* pre_pool,
+                const pdk_kv_pool* suf_pool, const void* q, int32_t q_dtype, int32_t Hq,
+                int32_t T, float sm_scale, float* out, float* lse_out, float* chunk_out,
+                float* chunk_lse, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!plan || !pre_pool || !suf_pool || !q || !out || !ws) return fail(PDK_ERR_ARG, "NULL argument");
+  if (T < 1 || Hq <= 0 || (long long)T * Hq > 0x7FFFFFFF)
+    return fail(PDK_ERR_ARG, "q_tokens %d, num_q_heads %d", T, Hq);
   if (plan->uploaded_to != ws)
     return fail(PDK_ERR_WORKSPACE, "plan was not uploaded to this workspace");
   if (pre_pool->page_size != plan->P || suf_pool->page_size != plan->Ps)
@@ -578,7 +586,8 @@ int pdk_run_chunked_decode(const pdk_chunked_plan* plan, const pdk_kv_pool* pre_
     return fail(PDK_ERR_SHAPE, "prefix and suffix pools disagree on heads or head dims");
   if ((!chunk_out) != (!chunk_lse)) return fail(PDK_ERR_ARG, "chunk_out/chunk_lse: both or neither");
   if (Hq <= 0 || Hq % pre_pool->num_kv_heads) return fail(PDK_ERR_SHAPE, "num_q_heads %d", Hq);
-  const ChunkedLayout L = chunked_layout(plan, Hq, Dv);
+  const int H = T * Hq;
+  const ChunkedLayout L = chunked_layout(plan, H, Dv);
   if (ws_bytes < L.total) return fail(PDK_ERR_WORKSPACE, "workspace %zu bytes < %zu", ws_bytes, L.total);
   const int32_t* base = (const int32_t*)ws;
   const auto& o = plan->off;
@@ -599,33 +608,34 @@ int pdk_run_chunked_decode(const pdk_chunked_plan* plan, const pdk_kv_pool* pre_
       pdk_csr vc{base + o.ch_indptr, base + o.ch_indices, base + o.ch_len, plan->n_chunks, 0};
       st = partial_rows(pre_pool, &vc, q, q_dtype, Hq, sm_scale, plan->S, base + o.ch_parts,
                         plan->n_pre_parts, base + o.ch_slots, base + o.ch_owner, 1, G,
-                        base + o.all_row_ch, v_all, l_all, stream);
+                        base + o.all_row_ch, v_all, l_all, stream, nullptr, T, 0);
       if (st) return st;
     }
     if (plan->n_suf_parts > 0) {
       pdk_csr vs{base + o.suf_indptr, base + o.suf_indices, base + o.suf_len, B, 0};
       st = partial_rows(suf_pool, &vs, q, q_dtype, Hq, sm_scale, plan->Ss, base + o.suf_parts,
                         plan->n_suf_parts, nullptr, nullptr, 0, G, base + o.all_row_suf, v_all,
-                        l_all, stream);
+                        l_all, stream, nullptr, T, 1);
       if (st) return st;
     }
     return merge_rows(v_all, l_all, plan->n_pre_parts + plan->n_suf_parts, base + o.all_req, B,
-                      Hq, Dv, out, lse_out, 1, stream);
+                      H, Dv, out, lse_out, 1, stream);
   }
   // chunk partials: each (request, chunk) is a view request with one member
   if (plan->n_pre_parts > 0) {
     pdk_csr vc{base + o.ch_indptr, base + o.ch_indices, base + o.ch_len, plan->n_chunks, 0};
     st = partial_rows(pre_pool, &vc, q, q_dtype, Hq, sm_scale, plan->S, base + o.ch_parts,
                       plan->n_pre_parts, base + o.ch_slots, base + o.ch_owner, 1, G,
-                      base + o.ch_parts, (float*)(w + L.v_pre), (float*)(w + L.l_pre), stream);
+                      base + o.ch_parts, (float*)(w + L.v_pre), (float*)(w + L.l_pre), stream,
+                      nullptr, T, 0);
     if (st) return st;
   }
   // each chunk's (O, LSE)
   st = merge_rows((float*)(w + L.v_pre), (float*)(w + L.l_pre), plan->n_pre_parts, base + o.ch_parts,
-                  plan->n_chunks, Hq, Dv, v_ch, l_ch, 1, stream);
+                  plan->n_chunks, H, Dv, v_ch, l_ch, 1, stream);
   if (st) return st;
   // across chunks -> even rows of the pair buffer
-  st = merge_rows(v_ch, l_ch, plan->n_chunks, base + o.req_chunks, B, Hq, Dv,
+  st = merge_rows(v_ch, l_ch, plan->n_chunks, base + o.req_chunks, B, H, Dv,
                   (float*)(w + L.v_pair), (float*)(w + L.l_pair), 2, stream);
   if (st) return st;
   // suffix partials and their merge -> odd rows
@@ -633,16 +643,38 @@ int pdk_run_chunked_decode(const pdk_chunked_plan* plan, const pdk_kv_pool* pre_
     pdk_csr vs{base + o.suf_indptr, base + o.suf_indices, base + o.suf_len, B, 0};
     st = partial_rows(suf_pool, &vs, q, q_dtype, Hq, sm_scale, plan->Ss, base + o.suf_parts,
                       plan->n_suf_parts, nullptr, nullptr, 0, G, base + o.suf_parts,
-                      (float*)(w + L.v_suf), (float*)(w + L.l_suf), stream);
+                      (float*)(w + L.v_suf), (float*)(w + L.l_suf), stream, nullptr, T, 1);
     if (st) return st;
   }
   st = merge_rows((float*)(w + L.v_suf), (float*)(w + L.l_suf), plan->n_suf_parts,
-                  base + o.suf_parts, B, Hq, Dv, (float*)(w + L.v_pair) + (size_t)Hq * Dv,
-                  (float*)(w + L.l_pair) + Hq, 2, stream);
+                  base + o.suf_parts, B, H, Dv, (float*)(w + L.v_pair) + (size_t)H * Dv,
+                  (float*)(w + L.l_pair) + H, 2, stream);
   if (st) return st;
   // prefix state with suffix state
-  return merge_rows((float*)(w + L.v_pair), (float*)(w + L.l_pair), 2 * B, base + o.pair, B, Hq,
+  return merge_rows((float*)(w + L.v_pair), (float*)(w + L.l_pair), 2 * B, base + o.pair, B, H,
                     Dv, out, lse_out, 1, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int pdk_run_chunked_decode(const pdk_chunked_plan* plan, const pdk_kv_pool* pre_pool,
+                           const pdk_kv_pool* suf_pool, const void* q, int32_t q_dtype,
+                           int32_t Hq, float sm_scale, float* out, float* lse_out,
+                           float* chunk_out, float* chunk_lse, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  return run_chunked(plan, pre_pool, suf_pool, q, q_dtype, Hq, 1, sm_scale, out, lse_out,
+                     chunk_out, chunk_lse, ws, ws_bytes, stream);
+}
+
+int pdk_run_chunked_multi_token(const pdk_chunked_plan* plan, const pdk_kv_pool* pre_pool,
+                                const pdk_kv_pool* suf_pool, const void* q, int32_t q_dtype,
+                                int32_t Hq, int32_t T, float sm_scale, float* out,
+                                float* lse_out, float* chunk_out, float* chunk_lse, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
+  return run_chunked(plan, pre_pool, suf_pool, q, q_dtype, Hq, T, sm_scale, out, lse_out,
+                     chunk_out, chunk_lse, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -1,0 +1,54 @@
+// Query rows of a partial launch: which batch query a row reads, where its
+// state goes, and which positions it sees. Included by the partial kernels.
+//
+// A workgroup serves the query rows of one (view request b, KV head h).
+// Row r is (n, g) = (r / G, r % G), query head h*G + g, and row group n is
+// (m, t) = (n / T, n % T): query token t (of the step's T >= 1 tokens) of
+//   * member m of the view request in a stacked view (level 0, or a chunk of
+//     a request's cached range): the query and the state rows are that
+//     member's own [cascade-PR, "The decomposition, and the one part that is
+//     not obvious": stacked heads kv*(M*G) + m*G + g map back to member m's
+//     head kv*G + g];
+//   * request b itself otherwise (m = 0).
+// Queries are q [*, T, Hq, Dk], states [*, T, Hq, Dv]. With causal masking
+// token t sits at position kv_len - T + t of the view request and sees
+// positions up to its own, so a partition past it contributes the empty
+// state [DCP-PR, section 3.2 figure: the new tokens' self-attention state is
+// merged with the cached chunks' states].
+#pragma once
+
+#include <limits.h>
+#include <stddef.h>
+
+#include "internal.h"
+
+namespace pdk {
+
+// Query rows of view request b per KV head.
+__device__ __forceinline__ int view_rows(const PartialArgs& a, bool stacked, int mbase, int b) {
+  return (stacked ? a.member_indptr[b + 1] - mbase : 1) * a.q_tokens * a.G;
+}
+
+// Batch query row (index into q viewed as [*, Hq, Dk]) of row group n.
+__device__ __forceinline__ int query_row(const PartialArgs& a, bool stacked, int mbase, int b,
+                                         int n) {
+  const int m = n / a.q_tokens, t = n - m * a.q_tokens;
+  return (stacked ? a.members[mbase + m] : b) * a.q_tokens + t;
+}
+
+// Index of (row group n, query head `head`) of partition p in the state
+// arrays v_out [*, Dv] / lse_out [*].
+__device__ __forceinline__ size_t state_index(const PartialArgs& a, bool stacked, int mbase,
+                                              int b, int p, int n, int head) {
+  const int m = n / a.q_tokens, t = n - m * a.q_tokens;
+  const int row = (stacked ? a.out_row_base[mbase + m] : a.out_row_base[b]) + p;
+  return ((size_t)row * a.q_tokens + t) * a.Hq + head;
+}
+
+// Exclusive end of the positions row group n sees (INT_MAX: the whole range).
+__device__ __forceinline__ int visible_end(const PartialArgs& a, int b, int n) {
+  if (!a.causal) return INT_MAX;
+  return a.kv_len[b] - a.q_tokens + n % a.q_tokens + 1;
+}
+
+}  // namespace pdk
