@@ -254,17 +254,25 @@ def bench_flat_mt(args, torch, pdk, W, dev, T=4):
                            "unique_kv_GBps": round(kv / (cold_us * 1e-6) / 1e9, 2)},
             "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                         "traffic": None,
-                         "kernel": f"multi-token partial ({T * b.group} rows per KV head)",
+                         "traffic": traffic_record("partial_dma.hip",
+                                                   f"llama3_8b_flat_{T}_token_causal_step"),
+                         "kernel": f"partial_dma_kernel<128,32,4,4> ({T * b.group} rows per "
+                                   "KV head)",
                          "kernel_us": round(t_part, 2), "bytes_per_launch": alg},
             "kernels_us": {"partials": round(t_part, 2), "merge": round(t_merge, 2)}}
 
 
-def bench_mla_mt(args, torch, pdk, W, dev):
-    """The MLA decode share with a 4-token step: every token sees the whole
-    fp8 cached prefix (chunks non-causal) and the bf16 suffix causally."""
-    T = 4
-    share = W.mla_share_with_query_tokens(W.mla_decode_share(), T, 1007)
+def bench_mla_mt(args, torch, pdk, W, dev, T=4, partition_tokens=4096,
+                 suffix_partition_tokens=256):
+    """The MLA decode share with a T = 4 token step: every token sees the
+    whole fp8 cached prefix (chunks non-causal) and the bf16 suffix
+    causally. Partitions of a whole chunk (4096 tokens) and of the whole
+    suffix (256): with four 128-row tiles per partition the grid is as wide
+    as the one-token step's, and the partial states to merge (1 MB per
+    partition) stay few."""
+    share = W.mla_share_with_query_tokens(
+        W.mla_decode_share(partition_tokens=partition_tokens,
+                           suffix_partition_tokens=suffix_partition_tokens), T, 1007)
     pre, suf = share.prefix, share.suffix
     p_pool, _, q = device_batch(torch, pdk, pre, dev)
     s_pool, _, _ = device_batch(torch, pdk, suf, dev)
@@ -296,7 +304,8 @@ def bench_mla_mt(args, torch, pdk, W, dev):
                        "head_dim_k": pre.head_dim_k, "head_dim_v": Dv,
                        "page_size": pre.page_size, "chunk_tokens": share.chunk_tokens,
                        "partition_tokens": pre.partition_tokens,
-                       "suffix_tokens": int(suf.kv_len[0])},
+                       "suffix_tokens": int(suf.kv_len[0]),
+                       "suffix_partition_tokens": suf.partition_tokens},
             "us_per_step": round(wall_ms * 1000, 2), "step_device_us": round(step_us, 2),
             "cold_cache": {"us_per_step": round(cold_us, 2)},
             "kv_bytes": kv_bytes, "flops_per_step": flops_step,
@@ -333,13 +342,16 @@ def kernel_source_sha(kernel_source):
     return h.hexdigest()
 
 
-def traffic_record(kernel_source, launches_per_step=1):
-    """HBM bytes per launch from the committed rocprofv3 counter record,
-    or None when the kernel's sources have changed since it was taken."""
+def traffic_record(kernel_source, workload=None):
+    """HBM bytes per launch from the committed rocprofv3 counter record of
+    the kernel (under its source file name, or "<source>|<workload>" for a
+    second workload of one kernel), or None when the kernel's sources have
+    changed since it was taken."""
     rec_path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(rec_path):
         return None
-    rec = json.load(open(rec_path)).get(kernel_source)
+    key = kernel_source if workload is None else f"{kernel_source}|{workload}"
+    rec = json.load(open(rec_path)).get(key)
     sha = kernel_source_sha(kernel_source)
     if not rec or sha is None or rec.get("source_sha256") != sha:
         return None
