@@ -145,6 +145,7 @@ def cpu_baseline(batches, budget_s=15.0):
 
 
 def planned(torch, pdk, b, params, dev):
+    """The plan, uploaded, and the host time of building it (us)."""
     plan = pdk.CascadePlan(b.indptr, b.indices, b.kv_len, b.page_size, params)
     t0 = time.perf_counter()
     plan2 = pdk.CascadePlan(b.indptr, b.indices, b.kv_len, b.page_size, params)
@@ -152,6 +153,17 @@ def planned(torch, pdk, b, params, dev):
     del plan2
     plan.upload(b.num_q_heads, b.head_dim_v, dev)
     return plan, plan_us
+
+
+def plan_cache_hit_us(pdk, b, params, reps=200):
+    """Host time of a plan-cache lookup that hits (the key hashed and
+    compared): what every layer after the first pays for its plan."""
+    cache = pdk.PlanCache(2)
+    cache.get(b.indptr, b.indices, b.kv_len, b.page_size, params)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        cache.get(b.indptr, b.indices, b.kv_len, b.page_size, params)
+    return (time.perf_counter() - t0) * 1e6 / reps
 
 
 def run_plan_steps(args, torch, pdk, b, pool, q, plan, dev):
@@ -535,7 +547,9 @@ def bench_cascade_arms(args, torch, pdk, W, dev):
                       "cold_cache_us_per_step": round(cold_us, 2),
                       "unique_kv_GBps": round(kv / (wall_ms * 1e-3) / 1e9, 2),
                       "frac_of_peak": round(kv / (wall_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                      "plan_host_us": round(plan_us, 1), "members": stats["members"],
+                      "plan_host_us": round(plan_us, 1),
+                      "plan_cache_hit_us": round(plan_cache_hit_us(pdk, b, params), 1),
+                      "members": stats["members"],
                       "shared_pages": stats["shared_pages"], "decline": decline}
         del plan
     return {"workload": "cascade_shared_prefix_b72", "unique_kv_bytes": kv,

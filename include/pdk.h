@@ -286,6 +286,29 @@ int pdk_cascade_plan_get(const pdk_cascade_plan* plan, int32_t field, const int3
  * decline receives a pdk_decline. Either pointer may be NULL. */
 int pdk_cascade_plan_stats(const pdk_cascade_plan* plan, int32_t stats[6], int32_t* decline);
 
+/* Plan memoization [cascade-PR, "What I left out, and where I was unsure":
+ * detection re-runs per layer per step; a plan slot in the plan cache is the
+ * follow-up]. A cache of up to `capacity` plans, least recently used out
+ * first. The key is the whole HOST page table - indptr, indices AND kv_len -
+ * with the page size and the parameters: a plan depends on the KV lengths,
+ * not only on the rows [FreeToken issue "Layer-major prefill for offloaded
+ * MoE": a plan cache keyed by rows was wrong once split-KV depended on KV
+ * length]. pdk_plan_cache_get returns the cached plan for an equal key
+ * (*hit = 1; content compared, not only hashed) or builds, caches and
+ * returns a new one (*hit = 0). The plan is owned by the cache: do not free
+ * it; it stays valid until a later get evicts it or the cache is freed, and
+ * keeps its upload, so every layer of a step runs it from the same
+ * workspace. *entry_id (may be NULL) is unique per built plan. Calls on one
+ * cache are serialized by a mutex. Errors: as pdk_cascade_plan_create. */
+typedef struct pdk_plan_cache pdk_plan_cache;
+int pdk_plan_cache_create(int32_t capacity, pdk_plan_cache** cache_out);
+void pdk_plan_cache_free(pdk_plan_cache* cache);
+int pdk_plan_cache_get(pdk_plan_cache* cache, const pdk_csr* csr_host, int32_t page_size,
+                       const pdk_cascade_params* params, pdk_cascade_plan** plan_out,
+                       int64_t* entry_id, int32_t* hit);
+/* stats = {lookups, hits, builds, evictions, entries} */
+int pdk_plan_cache_stats(const pdk_plan_cache* cache, int64_t stats[5]);
+
 /* Device workspace for pdk_run_cascade_decode: the plan's integer arrays
  * followed by the partial states of both levels. */
 size_t pdk_cascade_workspace_bytes(const pdk_cascade_plan* plan, int32_t num_q_heads,

@@ -14,6 +14,7 @@ request "[feat][DCP] Optimize MLA DCP (Enable Prefix Cache / Chunked Prefill
 """
 from __future__ import annotations
 
+import collections
 import ctypes
 import math
 import os
@@ -25,6 +26,7 @@ import torch
 
 __all__ = [
     "PdkError", "lib", "KVPool", "DeviceCSR", "CascadeParams", "CascadePlan", "ChunkedPlan",
+    "PlanCache",
     "partition_indptr", "validate_csr", "parse_switch", "cascade_enabled_from_env",
     "stacked_head_map", "paged_decode_partial", "merge_states", "decode_flat",
     "paged_multi_token_partial", "multi_token_flat",
@@ -100,6 +102,10 @@ _SIGS = {
     "pdk_chunked_workspace_bytes": (_S, [_P, _I, _I]),
     "pdk_chunked_plan_upload": (_I, [_P, _P, _S, _P]),
     "pdk_run_chunked_decode": (_I, [_P, _P, _P, _P, _I, _I, _F, _P, _P, _P, _P, _P, _S, _P]),
+    "pdk_plan_cache_create": (_I, [_I, _P]),
+    "pdk_plan_cache_free": (None, [_P]),
+    "pdk_plan_cache_get": (_I, [_P, _P, _I, _P, _P, _P, _P]),
+    "pdk_plan_cache_stats": (_I, [_P, _P]),
     "pdk_paged_multi_token_partial": (_I, [_P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _I, _P, _P,
                                            _P]),
     "pdk_multi_token_flat": (_I, [_P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _I, _P, _P, _P, _S,
@@ -409,11 +415,23 @@ class CascadePlan:
         _check(lib().pdk_cascade_plan_create(ctypes.byref(s), int(page_size), ctypes.byref(p),
                                              ctypes.byref(h)))
         self._h = h
+        self._owner = None
         self.params = params
         self.workspace = None
 
+    @classmethod
+    def _borrowed(cls, handle, params, owner):
+        """A plan owned by a PlanCache (not freed by this object)."""
+        self = cls.__new__(cls)
+        self._h = handle
+        self._owner = owner
+        self.params = params
+        self.workspace = None
+        return self
+
     def __del__(self):
-        if getattr(self, "_h", None) and _lib is not None:
+        if getattr(self, "_h", None) and getattr(self, "_owner", None) is None and \
+                _lib is not None:
             _lib.pdk_cascade_plan_free(self._h)
             self._h = None
 
@@ -485,6 +503,49 @@ class CascadePlan:
 # --------------------------------------------------------------------------
 # Chunked cached prefix + new suffix
 # --------------------------------------------------------------------------
+
+class PlanCache:
+    """Memoized cascade plans keyed by the whole page table (rows and KV
+    lengths), page size and parameters; least recently used out first. The
+    plan objects it returns keep their uploaded workspace across gets."""
+
+    def __init__(self, capacity: int = 8):
+        h = ctypes.c_void_p()
+        _check(lib().pdk_plan_cache_create(int(capacity), ctypes.byref(h)))
+        self._h = h
+        self.capacity = int(capacity)
+        # the C cache's entries, mirrored in the same LRU order: entry id -> plan
+        self._plans = collections.OrderedDict()
+
+    def __del__(self):
+        if getattr(self, "_h", None) and _lib is not None:
+            self._plans.clear()
+            _lib.pdk_plan_cache_free(self._h)
+            self._h = None
+
+    def get(self, indptr, indices, kv_len, page_size: int, params: CascadeParams):
+        """(plan, hit) for this page table."""
+        s, keep = _host_csr(indptr, indices, kv_len)
+        p = params.struct()
+        h = ctypes.c_void_p()
+        eid = ctypes.c_int64()
+        hit = ctypes.c_int32()
+        _check(lib().pdk_plan_cache_get(self._h, ctypes.byref(s), int(page_size), ctypes.byref(p),
+                                        ctypes.byref(h), ctypes.byref(eid), ctypes.byref(hit)))
+        key = eid.value
+        if key in self._plans:
+            self._plans.move_to_end(key)
+        else:
+            self._plans[key] = CascadePlan._borrowed(h, params, self)
+            while len(self._plans) > self.capacity:
+                self._plans.popitem(last=False)
+        return self._plans[key], bool(hit.value)
+
+    def stats(self):
+        st = (ctypes.c_int64 * 5)()
+        _check(lib().pdk_plan_cache_stats(self._h, st))
+        return dict(zip(("lookups", "hits", "builds", "evictions", "entries"), list(st)))
+
 
 class ChunkedPlan:
     def __init__(self, prefix_csr, prefix_page_size: int, chunk_tokens: int,

@@ -84,6 +84,32 @@ def test_fused_levels_equal_two_launches(gpu, case):
     assert_lse(res[1][1], rl, "fused cascade lse")
 
 
+def test_cached_plan_runs_like_a_fresh_one(gpu):
+    """Plans from the plan cache (one per page table, reused by every layer)
+    give the same outputs as freshly built plans, bit for bit, and a
+    changed KV length gets its own plan."""
+    b = W.cascade_shared_prefix(seed=2008, groups=2, members=6, prefix_tokens=768,
+                                suffix_max=200, extra=2, extra_tokens=300)
+    pool, csr, q = to_device(b)
+    params = gpu.CascadeParams(enabled=1, max_groups=0, l0_partition_tokens=256,
+                               l1_partition_tokens=256)
+    cache = gpu.PlanCache(4)
+    outs = []
+    for layer in range(3):
+        plan, hit = cache.get(b.indptr, b.indices, b.kv_len, b.page_size, params)
+        assert hit == (layer > 0)
+        o, l = plan.run(pool, q, b.sm_scale)
+        torch.cuda.synchronize()
+        outs.append((o.cpu().numpy(), l.cpu().numpy()))
+    fo, fl, _ = cascade(gpu, b, params, pool, q)
+    for o, l in outs:
+        assert np.array_equal(o, fo) and np.array_equal(l, fl)
+    kl = b.kv_len.copy()
+    kl[0] -= 1
+    plan, hit = cache.get(b.indptr, b.indices, kl, b.page_size, params)
+    assert not hit
+
+
 def test_declined_plan_runs_flat(gpu):
     b = W.llama3_8b_flat(seed=2005, batch=5, min_len=100, max_len=900)
     pool, csr, q = to_device(b)
