@@ -520,7 +520,8 @@ def bench_cascade_arms(args, torch, pdk, W, dev):
     """Shared-prefix workload (batch 72: 4 groups x 16 members sharing 4096
     tokens, private suffixes U[64,1024], 8 non-members of 2048 tokens): flat,
     the page's single-subgroup cascade, and every qualifying group (both
-    levels in one grid, and as two launches)."""
+    levels in one grid, as two launches, and with the partition sizes the
+    autotuner picks for the shape bucket on a cold cache)."""
     b = W.cascade_shared_prefix()
     pool, csr, q = device_batch(torch, pdk, b, dev)
     kv = b.unique_kv_bytes()
@@ -535,7 +536,21 @@ def bench_cascade_arms(args, torch, pdk, W, dev):
                                                      l1_partition_tokens=512)),
             ("cascade_all_groups_two_launches",
              pdk.CascadeParams(enabled=1, max_groups=0, l0_partition_tokens=256,
-                               l1_partition_tokens=512, fuse_levels=0))):
+                               l1_partition_tokens=512, fuse_levels=0)),
+            ("cascade_all_groups_autotuned", None)):
+        tuning = None
+        if params is None:
+            # the autotuner's choice for this shape bucket (measured here,
+            # outside the timed steps)
+            t0 = time.perf_counter()
+            params, info = pdk.cascade_autotune(
+                b.indptr, b.indices, b.kv_len, b.page_size,
+                pdk.CascadeParams(enabled=1, max_groups=0), pool, q, b.sm_scale,
+                [256, 512, 1024, 2048], [256, 512, 1024], reps=5)
+            tuning = {"l0_partition_tokens": params.l0_partition_tokens,
+                      "l1_partition_tokens": params.l1_partition_tokens,
+                      "tuned_cold_us": round(info["us"], 2), "measured": info["measured"],
+                      "tuning_s": round(time.perf_counter() - t0, 3)}
         plan, plan_us = planned(torch, pdk, b, params, dev)
         wall_ms, t_part, t_merge, cold_us = run_plan_steps(args, torch, pdk, b, pool, q, plan,
                                                            dev)
@@ -549,7 +564,7 @@ def bench_cascade_arms(args, torch, pdk, W, dev):
                       "frac_of_peak": round(kv / (wall_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                       "plan_host_us": round(plan_us, 1),
                       "plan_cache_hit_us": round(plan_cache_hit_us(pdk, b, params), 1),
-                      "members": stats["members"],
+                      "members": stats["members"], "tuning": tuning,
                       "shared_pages": stats["shared_pages"], "decline": decline}
         del plan
     return {"workload": "cascade_shared_prefix_b72", "unique_kv_bytes": kv,

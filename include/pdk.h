@@ -309,6 +309,54 @@ int pdk_plan_cache_get(pdk_plan_cache* cache, const pdk_csr* csr_host, int32_t p
 /* stats = {lookups, hits, builds, evictions, entries} */
 int pdk_plan_cache_stats(const pdk_plan_cache* cache, int64_t stats[5]);
 
+/* Partition-size autotuning per shape bucket, cold cache [cascade-PR, "What
+ * I left out, and where I was unsure": the shape-bucketed autotuner with
+ * cold-L2 methodology is not wired to either cascade level, which use the
+ * heuristic chunk size]. pdk_cascade_autotune builds the plan of every
+ * candidate (level-0 size x level-1 size, each a positive multiple of
+ * page_size), uploads it to `workspace` (at least
+ * pdk_cascade_autotune_workspace_bytes) and times `reps` whole steps
+ * (pdk_run_cascade_decode) on `stream` with HIP events, each after a read of
+ * `flush_buffer` (device scratch of flush_bytes, e.g. 512 MiB, > the 256 MB
+ * last-level cache; NULL: no flush), after two untimed steps. The fastest
+ * pair is kept for the step's shape bucket (pdk_cascade_tuning_key: page
+ * size, head counts and dims, dtypes, the plan's thresholds and switches,
+ * and power-of-two buckets of batch, total tokens, shared tokens and
+ * members); a later call in the same bucket returns it without measuring
+ * (result->measured = 0). times_us (optional, [n_l0 * n_l1], l0-major) gets
+ * each candidate's mean device us (-1 when nothing was measured). out /
+ * lse_out receive the last candidate's outputs. Synchronizes `stream`.
+ * pdk_cascade_tuned_params fills *tuned with the bucket's sizes (*found = 1)
+ * or copies *params (*found = 0). The bucket table is process-wide and
+ * guarded by a mutex; pdk_cascade_tuning_clear empties it. */
+typedef struct {
+  int32_t l0_partition_tokens;
+  int32_t l1_partition_tokens;
+  float us;         /* mean device microseconds per step of the chosen pair */
+  int32_t measured; /* 1: measured by this call; 0: from the bucket table */
+} pdk_tuning;
+int pdk_cascade_tuning_key(const pdk_csr* csr_host, int32_t page_size,
+                           const pdk_cascade_params* params, const pdk_kv_pool* pool,
+                           int32_t num_q_heads, int32_t q_dtype, int32_t key[16]);
+size_t pdk_cascade_autotune_workspace_bytes(const pdk_csr* csr_host, int32_t page_size,
+                                            const pdk_cascade_params* params,
+                                            const int32_t* l0_candidates, int32_t n_l0,
+                                            const int32_t* l1_candidates, int32_t n_l1,
+                                            int32_t num_q_heads, int32_t head_dim_v);
+int pdk_cascade_autotune(const pdk_csr* csr_host, int32_t page_size,
+                         const pdk_cascade_params* params, const pdk_kv_pool* pool, const void* q,
+                         int32_t q_dtype, int32_t num_q_heads, float sm_scale,
+                         const int32_t* l0_candidates, int32_t n_l0,
+                         const int32_t* l1_candidates, int32_t n_l1, int32_t reps,
+                         void* flush_buffer, size_t flush_bytes, void* workspace,
+                         size_t workspace_bytes, float* out, float* lse_out, float* times_us,
+                         hipStream_t stream, pdk_tuning* result);
+int pdk_cascade_tuned_params(const pdk_csr* csr_host, int32_t page_size,
+                             const pdk_cascade_params* params, const pdk_kv_pool* pool,
+                             int32_t num_q_heads, int32_t q_dtype, pdk_cascade_params* tuned,
+                             int32_t* found);
+void pdk_cascade_tuning_clear(void);
+
 /* Device workspace for pdk_run_cascade_decode: the plan's integer arrays
  * followed by the partial states of both levels. */
 size_t pdk_cascade_workspace_bytes(const pdk_cascade_plan* plan, int32_t num_q_heads,

@@ -15,6 +15,7 @@ request "[feat][DCP] Optimize MLA DCP (Enable Prefix Cache / Chunked Prefill
 from __future__ import annotations
 
 import collections
+import dataclasses
 import ctypes
 import math
 import os
@@ -26,7 +27,8 @@ import torch
 
 __all__ = [
     "PdkError", "lib", "KVPool", "DeviceCSR", "CascadeParams", "CascadePlan", "ChunkedPlan",
-    "PlanCache",
+    "PlanCache", "cascade_autotune", "cascade_tuned_params", "cascade_tuning_key",
+    "cascade_tuning_clear",
     "partition_indptr", "validate_csr", "parse_switch", "cascade_enabled_from_env",
     "stacked_head_map", "paged_decode_partial", "merge_states", "decode_flat",
     "paged_multi_token_partial", "multi_token_flat",
@@ -102,6 +104,12 @@ _SIGS = {
     "pdk_chunked_workspace_bytes": (_S, [_P, _I, _I]),
     "pdk_chunked_plan_upload": (_I, [_P, _P, _S, _P]),
     "pdk_run_chunked_decode": (_I, [_P, _P, _P, _P, _I, _I, _F, _P, _P, _P, _P, _P, _S, _P]),
+    "pdk_cascade_tuning_key": (_I, [_P, _I, _P, _P, _I, _I, _P]),
+    "pdk_cascade_autotune_workspace_bytes": (_S, [_P, _I, _P, _P, _I, _P, _I, _I, _I]),
+    "pdk_cascade_autotune": (_I, [_P, _I, _P, _P, _P, _I, _I, _F, _P, _I, _P, _I, _I, _P, _S,
+                                  _P, _S, _P, _P, _P, _P, _P]),
+    "pdk_cascade_tuned_params": (_I, [_P, _I, _P, _P, _I, _I, _P, _P]),
+    "pdk_cascade_tuning_clear": (None, []),
     "pdk_plan_cache_create": (_I, [_I, _P]),
     "pdk_plan_cache_free": (None, [_P]),
     "pdk_plan_cache_get": (_I, [_P, _P, _I, _P, _P, _P, _P]),
@@ -503,6 +511,80 @@ class CascadePlan:
 # --------------------------------------------------------------------------
 # Chunked cached prefix + new suffix
 # --------------------------------------------------------------------------
+
+class _Tuning(ctypes.Structure):
+    _fields_ = [("l0_partition_tokens", ctypes.c_int32), ("l1_partition_tokens", ctypes.c_int32),
+                ("us", ctypes.c_float), ("measured", ctypes.c_int32)]
+
+
+def _i32(values):
+    a = np.ascontiguousarray(values, dtype=np.int32)
+    return a, a.ctypes.data
+
+
+def cascade_tuning_key(indptr, indices, kv_len, page_size: int, params: CascadeParams,
+                       pool: KVPool, num_q_heads: int, q_dtype: int) -> tuple:
+    s, keep = _host_csr(indptr, indices, kv_len)
+    p, ps = params.struct(), pool.struct()
+    key = (ctypes.c_int32 * 16)()
+    _check(lib().pdk_cascade_tuning_key(ctypes.byref(s), int(page_size), ctypes.byref(p),
+                                        ctypes.byref(ps), int(num_q_heads), int(q_dtype), key))
+    return tuple(key)
+
+
+def cascade_autotune(indptr, indices, kv_len, page_size: int, params: CascadeParams,
+                     pool: KVPool, q: torch.Tensor, sm_scale: float, l0_candidates,
+                     l1_candidates, reps: int = 5, flush_bytes: int = 512 << 20, stream=None):
+    """Measure every (level-0, level-1) partition pair on a cold cache and
+    keep the fastest for the step's shape bucket. Returns (params with the
+    chosen sizes, dict with us / measured / per-candidate times)."""
+    s, keep = _host_csr(indptr, indices, kv_len)
+    p, ps = params.struct(), pool.struct()
+    c0, p0 = _i32(l0_candidates)
+    c1, p1 = _i32(l1_candidates)
+    B, Hq = int(q.shape[0]), int(q.shape[1])
+    Dv = pool.head_dim_v
+    need = int(lib().pdk_cascade_autotune_workspace_bytes(ctypes.byref(s), int(page_size),
+                                                          ctypes.byref(p), p0, len(c0), p1,
+                                                          len(c1), Hq, Dv))
+    if need == 0:
+        raise PdkError(-1, "autotune workspace query failed (candidates or table)")
+    ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    flush = torch.zeros(flush_bytes, dtype=torch.uint8, device=q.device) if flush_bytes else None
+    out = torch.empty((B, Hq, Dv), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    times = np.zeros(len(c0) * len(c1), dtype=np.float32)
+    res = _Tuning()
+    _check(lib().pdk_cascade_autotune(ctypes.byref(s), int(page_size), ctypes.byref(p),
+                                      ctypes.byref(ps), _ptr(q), _dtype_code(q), Hq,
+                                      float(sm_scale), p0, len(c0), p1, len(c1), int(reps),
+                                      _ptr(flush), int(flush_bytes if flush is not None else 0),
+                                      _ptr(ws), int(ws.numel()), _ptr(out), _ptr(lse),
+                                      times.ctypes.data, _stream(stream), ctypes.byref(res)))
+    tuned = dataclasses.replace(params, l0_partition_tokens=res.l0_partition_tokens,
+                                l1_partition_tokens=res.l1_partition_tokens)
+    return tuned, {"us": float(res.us), "measured": bool(res.measured),
+                   "times_us": times.reshape(len(c0), len(c1))}
+
+
+def cascade_tuned_params(indptr, indices, kv_len, page_size: int, params: CascadeParams,
+                         pool: KVPool, num_q_heads: int, q_dtype: int):
+    """(params with the bucket's tuned sizes, found)."""
+    s, keep = _host_csr(indptr, indices, kv_len)
+    p, ps = params.struct(), pool.struct()
+    out = _Params()
+    found = ctypes.c_int32()
+    _check(lib().pdk_cascade_tuned_params(ctypes.byref(s), int(page_size), ctypes.byref(p),
+                                          ctypes.byref(ps), int(num_q_heads), int(q_dtype),
+                                          ctypes.byref(out), ctypes.byref(found)))
+    tuned = dataclasses.replace(params, l0_partition_tokens=out.l0_partition_tokens,
+                                l1_partition_tokens=out.l1_partition_tokens)
+    return tuned, bool(found.value)
+
+
+def cascade_tuning_clear():
+    lib().pdk_cascade_tuning_clear()
+
 
 class PlanCache:
     """Memoized cascade plans keyed by the whole page table (rows and KV
