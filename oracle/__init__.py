@@ -22,6 +22,8 @@ What each module computes:
   planner    shared-prefix detection and the two-level cascade plan.
   cascade    the cascade composition (stacked level 0, level 1, pair merge).
   mla        the chunked cached-prefix / new-suffix composition.
+  nested     spans inside spans (system prompt, tenant sub-prefix, private
+             suffix) and their composition.
   multitoken T query tokens per request in one step (causal over the new
              tokens, non-causal over a cached prefix), their partials and
              merges, and the chunked split with T query tokens.
@@ -30,4 +32,4 @@ Every parity claim against the HIP path rests on these functions, which are in
 turn pinned by the not-GPU tests to closed forms, library routines, brute force
 and the invariants the pages state.
 """
-from . import codecs, attention, planner, cascade, mla, multitoken  # noqa: F401
+from . import codecs, attention, planner, cascade, mla, multitoken, nested  # noqa: F401

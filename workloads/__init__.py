@@ -341,6 +341,46 @@ def mla_decode_share(seed: int = 1005, batch: int = 32, heads: int = 128,
     return MlaShare(prefix=prefix, suffix=suffix, chunk_tokens=chunk_tokens)
 
 
+def nested_shared_prefix(seed: int = 1008, tenants: int = 4, members: int = 16,
+                         system_tokens: int = 2048, tenant_tokens: int = 2048,
+                         suffix_min: int = 64, suffix_max: int = 1024, extra: int = 8,
+                         extra_tokens: int = 2048, page_size: int = 16,
+                         poison: bool = True) -> PagedBatch:
+    """Nested sharing: every tenant's ``members`` requests start with the
+    same ``system_tokens`` pages, then the tenant's own ``tenant_tokens``
+    pages, then private suffixes U[suffix_min, suffix_max]; plus ``extra``
+    non-member requests of ``extra_tokens`` tokens. Batch slots are a seeded
+    shuffle. Heads, head dim, dtype and page as the flat Llama-3-8B
+    workload."""
+    rng = np.random.default_rng(seed)
+    P = page_size
+    assert system_tokens % P == 0 and tenant_tokens % P == 0
+    nxt = 0
+    system = list(range(nxt, nxt + system_tokens // P))
+    nxt += len(system)
+    seqs = []
+    for t in range(tenants):
+        sub = list(range(nxt, nxt + tenant_tokens // P))
+        nxt += len(sub)
+        for _ in range(members):
+            suf = int(rng.integers(suffix_min, suffix_max + 1))
+            npg = _pages(suf, P)
+            seqs.append((system + sub + list(range(nxt, nxt + npg)),
+                         system_tokens + tenant_tokens + suf))
+            nxt += npg
+    for _ in range(extra):
+        npg = _pages(extra_tokens, P)
+        seqs.append((list(range(nxt, nxt + npg)), extra_tokens))
+        nxt += npg
+    order = rng.permutation(len(seqs))
+    seqs = [seqs[i] for i in order]
+    return paged_batch_from_lists("nested_shared_prefix", rng, [s[0] for s in seqs],
+                                  [s[1] for s in seqs], page_size=P, num_q_heads=32,
+                                  num_kv_heads=8, head_dim_k=128, head_dim_v=128,
+                                  kv_dtype="bf16", q_dtype="bf16", partition_tokens=512,
+                                  poison=poison)
+
+
 # --------------------------------------------------------------------------
 # Multi-token query steps
 # --------------------------------------------------------------------------
