@@ -1,7 +1,7 @@
 """Benchmark: paged split-KV decode on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--workload flat|cascade|merge|mla|flat_mt|mla_mt|copy]
+                    [--workload flat|cascade|merge|mla|flat_mt|mla_mt|nested|copy]
 
 A step is one attention layer's decode for the whole batch: every partial
 launch and every merge of the path. Inputs are seeded synthetic tensors
@@ -516,36 +516,19 @@ def cascade_partial_bytes(b, plan):
     return b.unique_kv_bytes() + (members + b.batch) * q_row + tables + states, states
 
 
-def bench_cascade_arms(args, torch, pdk, W, dev):
-    """Shared-prefix workload (batch 72: 4 groups x 16 members sharing 4096
-    tokens, private suffixes U[64,1024], 8 non-members of 2048 tokens): flat,
-    the page's single-subgroup cascade, and every qualifying group (both
-    levels in one grid, as two launches, and with the partition sizes the
-    autotuner picks for the shape bucket on a cold cache)."""
-    b = W.cascade_shared_prefix()
-    pool, csr, q = device_batch(torch, pdk, b, dev)
+def run_arms(args, torch, pdk, b, pool, q, dev, arms_spec, tune_base=None, bytes_arm=None):
+    """Time each (name, params) arm on batch b; params None: the autotuner's
+    choice for the shape bucket, starting from tune_base (tuned outside the
+    timed steps). Returns the arms and, for bytes_arm, the algorithmic bytes
+    of its partial launch."""
     kv = b.unique_kv_bytes()
-    arms = {}
-    for name, params in (
-            ("flat", pdk.CascadeParams(enabled=0, l1_partition_tokens=512)),
-            ("cascade_single_group", pdk.CascadeParams(enabled=1, max_groups=1,
-                                                       l0_partition_tokens=512,
-                                                       l1_partition_tokens=512)),
-            ("cascade_all_groups", pdk.CascadeParams(enabled=1, max_groups=0,
-                                                     l0_partition_tokens=1024,
-                                                     l1_partition_tokens=512)),
-            ("cascade_all_groups_two_launches",
-             pdk.CascadeParams(enabled=1, max_groups=0, l0_partition_tokens=256,
-                               l1_partition_tokens=512, fuse_levels=0)),
-            ("cascade_all_groups_autotuned", None)):
+    arms, part = {}, (None, None)
+    for name, params in arms_spec:
         tuning = None
         if params is None:
-            # the autotuner's choice for this shape bucket (measured here,
-            # outside the timed steps)
             t0 = time.perf_counter()
             params, info = pdk.cascade_autotune(
-                b.indptr, b.indices, b.kv_len, b.page_size,
-                pdk.CascadeParams(enabled=1, max_groups=0), pool, q, b.sm_scale,
+                b.indptr, b.indices, b.kv_len, b.page_size, tune_base, pool, q, b.sm_scale,
                 [256, 512, 1024, 2048], [256, 512, 1024], reps=5)
             tuning = {"l0_partition_tokens": params.l0_partition_tokens,
                       "l1_partition_tokens": params.l1_partition_tokens,
@@ -555,8 +538,8 @@ def bench_cascade_arms(args, torch, pdk, W, dev):
         wall_ms, t_part, t_merge, cold_us = run_plan_steps(args, torch, pdk, b, pool, q, plan,
                                                            dev)
         stats, decline = plan.stats()
-        if name == "cascade_all_groups":
-            part_bytes, state_bytes = cascade_partial_bytes(b, plan)
+        if name == bytes_arm:
+            part = cascade_partial_bytes(b, plan)
         arms[name] = {"us_per_step": round(wall_ms * 1000, 2),
                       "partials_us": round(t_part, 2), "merge_us": round(t_merge, 2),
                       "cold_cache_us_per_step": round(cold_us, 2),
@@ -565,9 +548,34 @@ def bench_cascade_arms(args, torch, pdk, W, dev):
                       "plan_host_us": round(plan_us, 1),
                       "plan_cache_hit_us": round(plan_cache_hit_us(pdk, b, params), 1),
                       "members": stats["members"], "tuning": tuning,
+                      "spans": len(plan.field("span_pages")),
                       "shared_pages": stats["shared_pages"], "decline": decline}
         del plan
-    return {"workload": "cascade_shared_prefix_b72", "unique_kv_bytes": kv,
+    return arms, part
+
+
+def bench_cascade_arms(args, torch, pdk, W, dev):
+    """Shared-prefix workload (batch 72: 4 groups x 16 members sharing 4096
+    tokens, private suffixes U[64,1024], 8 non-members of 2048 tokens): flat,
+    the page's single-subgroup cascade, and every qualifying group (both
+    levels in one grid, as two launches, and with the partition sizes the
+    autotuner picks for the shape bucket on a cold cache)."""
+    b = W.cascade_shared_prefix()
+    pool, csr, q = device_batch(torch, pdk, b, dev)
+    arms, (part_bytes, state_bytes) = run_arms(args, torch, pdk, b, pool, q, dev, (
+        ("flat", pdk.CascadeParams(enabled=0, l1_partition_tokens=512)),
+        ("cascade_single_group", pdk.CascadeParams(enabled=1, max_groups=1,
+                                                   l0_partition_tokens=512,
+                                                   l1_partition_tokens=512)),
+        ("cascade_all_groups", pdk.CascadeParams(enabled=1, max_groups=0,
+                                                 l0_partition_tokens=1024,
+                                                 l1_partition_tokens=512)),
+        ("cascade_all_groups_two_launches",
+         pdk.CascadeParams(enabled=1, max_groups=0, l0_partition_tokens=256,
+                           l1_partition_tokens=512, fuse_levels=0)),
+        ("cascade_all_groups_autotuned", None)),
+        tune_base=pdk.CascadeParams(enabled=1, max_groups=0), bytes_arm="cascade_all_groups")
+    return {"workload": "cascade_shared_prefix_b72", "unique_kv_bytes": b.unique_kv_bytes(),
             "partial_launch_bytes": part_bytes, "partial_state_bytes": state_bytes,
             "flat_read_bytes": b.read_kv_bytes(), "arms": arms,
             "speedup_all_groups": round(arms["flat"]["us_per_step"] /
@@ -576,13 +584,61 @@ def bench_cascade_arms(args, torch, pdk, W, dev):
                                           arms["cascade_single_group"]["us_per_step"], 3)}
 
 
+def bench_nested(args, torch, pdk, W, dev):
+    """Nested sharing (batch 72: 4 tenants x 16 requests behind one 2048-token
+    system prompt, a 2048-token sub-prefix per tenant, private suffixes
+    U[64,1024], 8 unshared 2048-token requests): flat, one span level (the
+    system prompt; each tenant's sub-prefix read by every member), and the
+    tenant spans nested below it (every shared page read once), the last with
+    the sizes the autotuner picks. value = the nested arm's rate over unique
+    KV bytes."""
+    b = W.nested_shared_prefix()
+    pool, csr, q = device_batch(torch, pdk, b, dev)
+    base = pdk.CascadeParams(enabled=1, max_groups=0, max_depth=2)
+    arms, (part_bytes, state_bytes) = run_arms(args, torch, pdk, b, pool, q, dev, (
+        ("flat", pdk.CascadeParams(enabled=0, l1_partition_tokens=512)),
+        ("one_span_level", pdk.CascadeParams(enabled=1, max_groups=0, max_depth=1,
+                                             l0_partition_tokens=1024, l1_partition_tokens=512)),
+        ("nested_spans", pdk.CascadeParams(enabled=1, max_groups=0, max_depth=2,
+                                           l0_partition_tokens=1024, l1_partition_tokens=512)),
+        ("nested_spans_autotuned", None)), tune_base=base, bytes_arm="nested_spans")
+    best = arms["nested_spans"]
+    kv = b.unique_kv_bytes()
+    achieved = part_bytes / (best["partials_us"] * 1e-6) / 1e9
+    return {"metric": METRIC, "value": best["unique_kv_GBps"], "unit": "GB/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(best["us_per_step"] / 1000, 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "nested_shared_prefix_b72", "batch": 72, "tenants": 4,
+                       "members_per_tenant": 16, "system_tokens": 2048, "tenant_tokens": 2048,
+                       "suffix_tokens": "uniform[64,1024]", "extra_requests": 8,
+                       "extra_tokens": 2048, "num_q_heads": 32, "num_kv_heads": 8,
+                       "head_dim": 128, "page_size": 16},
+            "us_per_step": best["us_per_step"], "frac_of_peak": best["frac_of_peak"],
+            "cold_cache": {"us_per_step": best["cold_cache_us_per_step"],
+                           "unique_kv_GBps": round(kv / (best["cold_cache_us_per_step"] * 1e-6)
+                                                   / 1e9, 2)},
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "traffic": None,
+                         "kernel": "cascade_partial_kernel (spans + level 1 in one grid)",
+                         "kernel_us": best["partials_us"], "bytes_per_launch": part_bytes},
+            "partial_state_bytes": state_bytes, "unique_kv_bytes": kv,
+            "flat_read_bytes": b.read_kv_bytes(), "arms": arms,
+            "speedup_nested_vs_flat": round(arms["flat"]["us_per_step"] /
+                                            best["us_per_step"], 3),
+            "speedup_nested_vs_one_level": round(arms["one_span_level"]["us_per_step"] /
+                                                 best["us_per_step"], 3)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="flat",
-                    choices=["flat", "cascade", "merge", "mla", "copy", "flat_mt", "mla_mt"])
+                    choices=["flat", "cascade", "merge", "mla", "copy", "flat_mt", "mla_mt",
+                             "nested"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cascade", action="store_true")
     args = ap.parse_args()
@@ -598,8 +654,8 @@ def main():
         sys.exit(2)
     pdk.lib()
     res = {"flat": bench_flat, "cascade": bench_cascade, "merge": bench_merge, "mla": bench_mla,
-           "copy": bench_copy, "flat_mt": bench_flat_mt,
-           "mla_mt": bench_mla_mt}[args.workload](args, torch, pdk, W, "cuda:0")
+           "copy": bench_copy, "flat_mt": bench_flat_mt, "mla_mt": bench_mla_mt,
+           "nested": bench_nested}[args.workload](args, torch, pdk, W, "cuda:0")
     print(json.dumps(res), flush=True)
 
 

@@ -243,6 +243,10 @@ typedef struct {
                                   queries, head dim 128, pages >= 16 tokens,
                                   3-4 query heads per KV head), bit-identical
                                   to two launches; 0: two launches */
+  int32_t max_depth;           /* levels of shared spans: 1 (default) is the
+                                  page's one shared level; k > 1 adds nested
+                                  spans below a span (a tenant sub-prefix
+                                  under a system prompt), up to k levels */
 } pdk_cascade_params;
 
 void pdk_cascade_params_default(pdk_cascade_params* params);
@@ -256,15 +260,23 @@ typedef struct pdk_cascade_plan pdk_cascade_plan;
  * page or fall below the thresholds, selection by span*(members-1), ties to
  * the lowest first batch index. A declined plan is not an error: it returns
  * PDK_OK with a decline reason and runs the flat path. The plan is owned by
- * the library until pdk_cascade_plan_free. page_size must match the pool. */
+ * the library until pdk_cascade_plan_free. page_size must match the pool.
+ * With max_depth > 1, nested spans follow below each selected span [the
+ * page scopes a third level out in "What I left out"; merging is
+ * associative, "How the #898 merge kernel is reused"]: the span's members
+ * are grouped by their page at the span's end, and each subgroup passing the
+ * same checks from that page on is a child span; spans are numbered level by
+ * level (by first member within a level) and all of them form the level-0
+ * view; a request's level-1 range starts after the deepest span holding it
+ * and its merge group has one row per span holding it plus one. */
 int pdk_cascade_plan_create(const pdk_csr* csr_host, int32_t page_size,
                             const pdk_cascade_params* params, pdk_cascade_plan** plan_out);
 void pdk_cascade_plan_free(pdk_cascade_plan* plan);
 
 /* Read-only views of the plan's host arrays (valid until the plan is freed). */
 enum {
-  PDK_PLAN_MEMBERS = 0,         /* [total members] batch indices, level-0 order */
-  PDK_PLAN_GROUP_INDPTR = 1,    /* [K+1] offsets of each group into MEMBERS */
+  PDK_PLAN_MEMBERS = 0,         /* [member slots] batch indices, level-0 order */
+  PDK_PLAN_GROUP_INDPTR = 1,    /* [K+1] offsets of each span into MEMBERS */
   PDK_PLAN_SPAN_PAGES = 2,      /* [K] */
   PDK_PLAN_L0_INDPTR = 3,       /* [K+1] level-0 view */
   PDK_PLAN_L0_INDICES = 4,
@@ -272,11 +284,14 @@ enum {
   PDK_PLAN_L1_INDPTR = 6,       /* [B+1] level-1 view (= flat view when declined) */
   PDK_PLAN_L1_INDICES = 7,
   PDK_PLAN_L1_LEN = 8,          /* [B] */
-  PDK_PLAN_MERGE_INDPTR = 9,    /* [B+1] the page's pairing: 2 rows per member, else 1 */
+  PDK_PLAN_MERGE_INDPTR = 9,    /* [B+1] the page's pairing: 1 row per span holding
+                                   the request, plus 1 */
   PDK_PLAN_FUSED_MERGE_INDPTR = 10, /* [B+1] rows per request in the single merge */
-  PDK_PLAN_GROUP_OF = 11,       /* [B] level-0 group of each request, -1 if none */
-  PDK_PLAN_MEMBER_RANK = 12,    /* [B] rank within its group, -1 if none */
-  PDK_PLAN_NUM_FIELDS = 13
+  PDK_PLAN_GROUP_OF = 11,       /* [B] outermost span of each request, -1 if none */
+  PDK_PLAN_MEMBER_RANK = 12,    /* [B] rank within that span, -1 if none */
+  PDK_PLAN_SPAN_START = 13,     /* [K] first page of each span (0 for outermost) */
+  PDK_PLAN_SPAN_PARENT = 14,    /* [K] enclosing span, -1 for outermost */
+  PDK_PLAN_NUM_FIELDS = 15
 };
 int pdk_cascade_plan_get(const pdk_cascade_plan* plan, int32_t field, const int32_t** data,
                          int32_t* len);

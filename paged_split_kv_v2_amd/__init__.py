@@ -41,7 +41,8 @@ DECLINE_NAMES = {0: "none", 1: "disabled", 2: "no_candidate", 3: "members_below_
                  4: "span_below_min", 5: "reaches_last_page"}
 PLAN_FIELDS = {"members": 0, "group_indptr": 1, "span_pages": 2, "l0_indptr": 3,
                "l0_indices": 4, "l0_len": 5, "l1_indptr": 6, "l1_indices": 7, "l1_len": 8,
-               "merge_indptr": 9, "fused_merge_indptr": 10, "group_of": 11, "member_rank": 12}
+               "merge_indptr": 9, "fused_merge_indptr": 10, "group_of": 11, "member_rank": 12,
+               "span_start": 13, "span_parent": 14}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpdk.so")
@@ -71,7 +72,7 @@ class _Params(ctypes.Structure):
     _fields_ = [("enabled", ctypes.c_int32), ("min_shared_pages", ctypes.c_int32),
                 ("min_members", ctypes.c_int32), ("max_groups", ctypes.c_int32),
                 ("l0_partition_tokens", ctypes.c_int32), ("l1_partition_tokens", ctypes.c_int32),
-                ("fuse_levels", ctypes.c_int32)]
+                ("fuse_levels", ctypes.c_int32), ("max_depth", ctypes.c_int32)]
 
 
 _P, _I, _F, _S, _L = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t, ctypes.c_int64
@@ -407,10 +408,12 @@ class CascadeParams:
     l0_partition_tokens: int = 256
     l1_partition_tokens: int = 512
     fuse_levels: int = 1
+    max_depth: int = 1
 
     def struct(self) -> _Params:
         return _Params(self.enabled, self.min_shared_pages, self.min_members, self.max_groups,
-                       self.l0_partition_tokens, self.l1_partition_tokens, self.fuse_levels)
+                       self.l0_partition_tokens, self.l1_partition_tokens, self.fuse_levels,
+                       self.max_depth)
 
 
 class CascadePlan:

@@ -78,8 +78,9 @@ int make_key(const pdk_csr* csr, int32_t P, const pdk_cascade_params* pr, const 
   long long tokens = 0;
   for (int b = 0; b < csr->batch; ++b) tokens += csr->kv_len[b];
   *key = TuneKey{P, pool->num_kv_heads, Hq / pool->num_kv_heads, pool->head_dim_k,
-                 pool->head_dim_v, pool->dtype, q_dtype, pr->enabled, pr->max_groups,
-                 pr->fuse_levels, pr->min_shared_pages * 64 + pr->min_members,
+                 pool->head_dim_v, pool->dtype, q_dtype, pr->enabled,
+                 pr->max_groups * 64 + pr->max_depth, pr->fuse_levels,
+                 pr->min_shared_pages * 64 + pr->min_members,
                  log2_bucket(csr->batch), half_log2_bucket(tokens),
                  half_log2_bucket(stats[3]), log2_bucket(stats[1]), decline};
   return PDK_OK;

@@ -119,6 +119,7 @@ void pdk_cascade_params_default(pdk_cascade_params* p) {
   p->l0_partition_tokens = 256;
   p->l1_partition_tokens = 512;
   p->fuse_levels = 1;
+  p->max_depth = 1;
 }
 
 int pdk_cascade_plan_create(const pdk_csr* csr, int32_t P, const pdk_cascade_params* params,
@@ -135,6 +136,7 @@ int pdk_cascade_plan_create(const pdk_csr* csr, int32_t P, const pdk_cascade_par
     return fail(PDK_ERR_ARG, "partition sizes must be positive multiples of page_size %d", P);
   if (pr.fuse_levels != 0 && pr.fuse_levels != 1)
     return fail(PDK_ERR_ARG, "fuse_levels must be 0 or 1");
+  if (pr.max_depth < 1) return fail(PDK_ERR_ARG, "max_depth %d < 1", pr.max_depth);
 
   const int B = csr->batch;
   const int32_t* indptr = csr->indptr;
@@ -206,24 +208,82 @@ int pdk_cascade_plan_create(const pdk_csr* csr, int32_t P, const pdk_cascade_par
     }
   }
 
+  // Spans: the selected groups (depth 0), then level by level the child spans
+  // of nested sharing: below a span ending at page e, members grouped by
+  // their page at e; a subgroup passing the same checks as a group (member
+  // count, common prefix from e capped to full pages, span threshold, not
+  // reaching a member's last page) is a child span, ordered by first member.
+  struct SpanNode {
+    std::vector<int32_t> members;
+    int32_t start, span, depth, parent;
+  };
+  std::vector<SpanNode> nodes;
+  for (const auto& c : chosen) nodes.push_back({c.members, 0, c.span, 0, -1});
+  {
+    size_t lo = 0, hi = nodes.size();
+    for (int depth = 1; depth < pr.max_depth && lo < hi; ++depth) {
+      std::vector<SpanNode> next;
+      for (size_t i = lo; i < hi; ++i) {
+        const int32_t e = nodes[i].start + nodes[i].span;
+        std::map<int32_t, std::vector<int32_t>> by_page;
+        for (int32_t b : nodes[i].members)
+          if (indptr[b + 1] - indptr[b] > e) by_page[idx[indptr[b] + e]].push_back(b);
+        for (auto& kv : by_page) {
+          const auto& mem = kv.second;  // ascending batch order
+          if ((int)mem.size() < std::max(2, pr.min_members)) continue;
+          int32_t c = 0;
+          for (;;) {
+            bool ok = true;
+            for (int32_t b : mem)
+              if (e + c >= indptr[b + 1] - indptr[b] ||
+                  idx[indptr[b] + e + c] != idx[indptr[mem[0]] + e + c]) {
+                ok = false;
+                break;
+              }
+            if (!ok) break;
+            ++c;
+          }
+          for (int32_t b : mem) c = std::min(c, len[b] / P - e);
+          if (c < std::max(1, pr.min_shared_pages)) continue;
+          bool last = false;
+          for (int32_t b : mem) last = last || (e + c == indptr[b + 1] - indptr[b]);
+          if (last) continue;
+          next.push_back({mem, e, c, depth, (int32_t)i});
+        }
+      }
+      std::sort(next.begin(), next.end(),
+                [](const SpanNode& x, const SpanNode& y) { return x.members[0] < y.members[0]; });
+      lo = nodes.size();
+      nodes.insert(nodes.end(), next.begin(), next.end());
+      hi = nodes.size();
+    }
+  }
+
   auto& F = plan->f;
-  const int K = (int)chosen.size();
+  const int K = (int)nodes.size();
   plan->n_groups = K;
-  std::vector<int32_t> group_of(B, -1), rank(B, -1), span_of(B, 0);
+  std::vector<int32_t> group_of(B, -1), rank(B, -1), private_start(B, 0), n_spans(B, 0);
   F[PDK_PLAN_GROUP_INDPTR].push_back(0);
   F[PDK_PLAN_L0_INDPTR].push_back(0);
   for (int k = 0; k < K; ++k) {
-    const auto& c = chosen[k];
+    const auto& c = nodes[k];
     for (size_t m = 0; m < c.members.size(); ++m) {
-      group_of[c.members[m]] = k;
-      rank[c.members[m]] = (int32_t)m;
-      span_of[c.members[m]] = c.span;
-      F[PDK_PLAN_MEMBERS].push_back(c.members[m]);
+      const int32_t b = c.members[m];
+      if (c.depth == 0) {
+        group_of[b] = k;
+        rank[b] = (int32_t)m;
+      }
+      // spans are laid out level by level, so the last one seen is the deepest
+      private_start[b] = c.start + c.span;
+      ++n_spans[b];
+      F[PDK_PLAN_MEMBERS].push_back(b);
     }
     F[PDK_PLAN_GROUP_INDPTR].push_back((int32_t)F[PDK_PLAN_MEMBERS].size());
     F[PDK_PLAN_SPAN_PAGES].push_back(c.span);
+    F[PDK_PLAN_SPAN_START].push_back(c.start);
+    F[PDK_PLAN_SPAN_PARENT].push_back(c.parent);
     const int b0 = c.members[0];
-    for (int i = 0; i < c.span; ++i) F[PDK_PLAN_L0_INDICES].push_back(idx[indptr[b0] + i]);
+    for (int i = 0; i < c.span; ++i) F[PDK_PLAN_L0_INDICES].push_back(idx[indptr[b0] + c.start + i]);
     F[PDK_PLAN_L0_INDPTR].push_back((int32_t)F[PDK_PLAN_L0_INDICES].size());
     F[PDK_PLAN_L0_LEN].push_back(c.span * P);
     plan->max_members = std::max(plan->max_members, (int32_t)c.members.size());
@@ -231,11 +291,11 @@ int pdk_cascade_plan_create(const pdk_csr* csr, int32_t P, const pdk_cascade_par
   F[PDK_PLAN_L1_INDPTR].push_back(0);
   F[PDK_PLAN_MERGE_INDPTR].push_back(0);
   for (int b = 0; b < B; ++b) {
-    const int s = span_of[b];
+    const int s = private_start[b];
     for (int i = indptr[b] + s; i < indptr[b + 1]; ++i) F[PDK_PLAN_L1_INDICES].push_back(idx[i]);
     F[PDK_PLAN_L1_INDPTR].push_back((int32_t)F[PDK_PLAN_L1_INDICES].size());
     F[PDK_PLAN_L1_LEN].push_back(len[b] - s * P);
-    F[PDK_PLAN_MERGE_INDPTR].push_back(F[PDK_PLAN_MERGE_INDPTR].back() + (group_of[b] >= 0 ? 2 : 1));
+    F[PDK_PLAN_MERGE_INDPTR].push_back(F[PDK_PLAN_MERGE_INDPTR].back() + n_spans[b] + 1);
   }
   F[PDK_PLAN_GROUP_OF] = group_of;
   F[PDK_PLAN_MEMBER_RANK] = rank;
@@ -253,21 +313,29 @@ int pdk_cascade_plan_create(const pdk_csr* csr, int32_t P, const pdk_cascade_par
                                    std::max(1, ceil_div(F[PDK_PLAN_L1_LEN][b], S1)));
   plan->n_l0_parts = plan->l0_part_indptr.back();
   plan->n_l1_parts = plan->l1_part_indptr.back();
+  // each request's rows: one block of partitions per span holding it
+  // (outermost first), then its level-1 partitions
   auto& fused = F[PDK_PLAN_FUSED_MERGE_INDPTR];
   fused.assign(1, 0);
   plan->l1_row_base.resize(B);
-  std::vector<int32_t> row_start(B);
+  std::vector<int32_t> next_row(B);
+  std::vector<int32_t> span_rows(B, 0);
+  for (int k = 0; k < K; ++k)
+    for (int32_t b : nodes[k].members)
+      span_rows[b] += plan->l0_part_indptr[k + 1] - plan->l0_part_indptr[k];
   for (int b = 0; b < B; ++b) {
-    const int k = group_of[b];
-    const int n0 = k >= 0 ? plan->l0_part_indptr[k + 1] - plan->l0_part_indptr[k] : 0;
     const int n1 = plan->l1_part_indptr[b + 1] - plan->l1_part_indptr[b];
-    row_start[b] = fused.back();
-    plan->l1_row_base[b] = fused.back() + n0;
-    fused.push_back(fused.back() + n0 + n1);
+    next_row[b] = fused.back();
+    plan->l1_row_base[b] = fused.back() + span_rows[b];
+    fused.push_back(fused.back() + span_rows[b] + n1);
   }
   plan->total_rows = fused.back();
   plan->member_row_base.clear();
-  for (int32_t b : F[PDK_PLAN_MEMBERS]) plan->member_row_base.push_back(row_start[b]);
+  for (int k = 0; k < K; ++k)
+    for (int32_t b : nodes[k].members) {
+      plan->member_row_base.push_back(next_row[b]);
+      next_row[b] += plan->l0_part_indptr[k + 1] - plan->l0_part_indptr[k];
+    }
 
   long long shared = 0, pre_chunks = 0, suf_chunks = 0;
   for (int k = 0; k < K; ++k) {
@@ -275,8 +343,10 @@ int pdk_cascade_plan_create(const pdk_csr* csr, int32_t P, const pdk_cascade_par
     pre_chunks += ceil_div((long long)F[PDK_PLAN_SPAN_PAGES][k] * P, S0);
   }
   for (int b = 0; b < B; ++b) suf_chunks += ceil_div(F[PDK_PLAN_L1_LEN][b], S1);
+  int32_t distinct = 0;
+  for (int b = 0; b < B; ++b) distinct += n_spans[b] > 0;
   plan->stats[0] = B;
-  plan->stats[1] = (int32_t)F[PDK_PLAN_MEMBERS].size();
+  plan->stats[1] = distinct;
   plan->stats[2] = (int32_t)shared;
   plan->stats[3] = (int32_t)(shared * P);
   plan->stats[4] = (int32_t)pre_chunks;

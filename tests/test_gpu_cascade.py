@@ -110,6 +110,32 @@ def test_cached_plan_runs_like_a_fresh_one(gpu):
     assert not hit
 
 
+@pytest.mark.parametrize("depth", [1, 2, 3])
+def test_nested_sharing(gpu, depth):
+    """A system prompt shared by every tenant's requests and a sub-prefix per
+    tenant: one span level (the page's), or the tenant spans nested below it,
+    all in the one level-0 launch; equal to the oracle and to the flat
+    launch, and the same with both levels in one grid or two launches."""
+    b = W.nested_shared_prefix(seed=2510, tenants=3, members=5, system_tokens=512,
+                               tenant_tokens=256, suffix_max=300, extra=3, extra_tokens=600)
+    pool, csr, q = to_device(b)
+    res = {}
+    for fuse in (1, 0):
+        params = gpu.CascadeParams(enabled=1, max_groups=0, max_depth=depth, fuse_levels=fuse,
+                                   l0_partition_tokens=256, l1_partition_tokens=256)
+        out, lse, plan = cascade(gpu, b, params, pool, q)
+        assert len(plan.field("span_pages")) == (1 if depth == 1 else 4)
+        res[fuse] = (out, lse)
+    assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][1], res[1][1])
+    out, lse = res[1]
+    ro, rl = oatt.decode_attention(b)
+    assert_close(out, ro, TOL["bf16"], "nested cascade out")
+    assert_lse(lse, rl, "nested cascade lse")
+    fo, fl, _ = flat_decode(b, pool, csr, q, 256)
+    assert rel_err(out, fo.cpu().numpy()) <= 1e-5
+    assert lse_err(lse, fl.cpu().numpy()) <= 1e-5
+
+
 def test_declined_plan_runs_flat(gpu):
     b = W.llama3_8b_flat(seed=2005, batch=5, min_len=100, max_len=900)
     pool, csr, q = to_device(b)

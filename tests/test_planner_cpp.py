@@ -89,3 +89,70 @@ def test_invalid_plan_arguments():
     with pytest.raises(pdk.PdkError):
         pdk.CascadePlan([0, 1], [3], [16], 16,
                         pdk.CascadeParams(enabled=1, l1_partition_tokens=24))
+
+
+def nested_expected(indptr, indices, kv_len, P, params, depth):
+    """The arrays the library's plan must hold, from the oracle's nested plan."""
+    from oracle import nested
+    ref = nested.build_nested_plan(indptr, indices, kv_len, P, params, depth)
+    B = len(kv_len)
+    members, gptr, l0_idx, l0_ptr = [], [0], [], [0]
+    for sp in ref.spans:
+        members += sp.members
+        gptr.append(len(members))
+        b0 = sp.members[0]
+        l0_idx += list(indices[indptr[b0] + sp.start_page:indptr[b0] + sp.start_page + sp.span_pages])
+        l0_ptr.append(len(l0_idx))
+    group_of, rank = [-1] * B, [-1] * B
+    for k, sp in enumerate(ref.spans):
+        if sp.depth == 0:
+            for m, b in enumerate(sp.members):
+                group_of[b], rank[b] = k, m
+    l1_idx, l1_ptr, l1_len = [], [0], []
+    for b in range(B):
+        s = int(ref.private_start_page[b])
+        l1_idx += list(indices[indptr[b] + s:indptr[b + 1]])
+        l1_ptr.append(len(l1_idx))
+        l1_len.append(int(kv_len[b]) - s * P)
+    return ref, {"members": members, "group_indptr": gptr,
+                 "span_pages": [s.span_pages for s in ref.spans],
+                 "span_start": [s.start_page for s in ref.spans],
+                 "span_parent": [s.parent for s in ref.spans],
+                 "l0_indptr": l0_ptr, "l0_indices": l0_idx,
+                 "l0_len": [s.span_pages * P for s in ref.spans],
+                 "l1_indptr": l1_ptr, "l1_indices": l1_idx, "l1_len": l1_len,
+                 "merge_indptr": ref.merge_indptr, "group_of": group_of, "member_rank": rank}
+
+
+@pytest.mark.parametrize("depth", [2, 3])
+def test_nested_plans_match_the_oracle(depth):
+    from workloads import nested_shared_prefix
+    cases = []
+    for seed in range(2500, 2504):
+        b = nested_shared_prefix(seed=seed, tenants=3, members=4, system_tokens=64,
+                                 tenant_tokens=48, suffix_min=1, suffix_max=40, extra=2,
+                                 extra_tokens=50, page_size=8, poison=False)
+        cases.append((b.indptr, b.indices, b.kv_len, 8))
+    b = nested_shared_prefix(poison=False)
+    cases.append((b.indptr, b.indices, b.kv_len, 16))
+    for indptr, indices, kv_len, P in cases:
+        kw = dict(enabled=1, min_shared_pages=1, max_groups=0, l0_partition_tokens=4 * P,
+                  l1_partition_tokens=8 * P)
+        ref, want = nested_expected(indptr, indices, kv_len, P, oplan.CascadeParams(**kw), depth)
+        assert sum(s.depth > 0 for s in ref.spans) > 0
+        plan = pdk.CascadePlan(indptr, indices, kv_len, P, pdk.CascadeParams(max_depth=depth, **kw))
+        for f, v in want.items():
+            assert np.array_equal(plan.field(f).astype(np.int64), np.asarray(v, np.int64)), f
+        stats, decline = plan.stats()
+        S0, S1 = kw["l0_partition_tokens"], kw["l1_partition_tokens"]
+        assert decline == ref.decline
+        assert stats["members"] == sum(1 for s in ref.spans_of if s)
+        assert stats["shared_pages"] == sum(s.span_pages for s in ref.spans)
+        assert stats["prefix_chunks"] == sum(-(-s.span_pages * P // S0) for s in ref.spans)
+        assert stats["suffix_chunks"] == sum(-(-int(n) // S1) for n in want["l1_len"])
+
+
+def test_max_depth_is_validated():
+    b = tiny_gqa_fp32()
+    with pytest.raises(pdk.PdkError):
+        pdk.CascadePlan(b.indptr, b.indices, b.kv_len, 16, pdk.CascadeParams(enabled=1, max_depth=0))
