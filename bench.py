@@ -620,7 +620,8 @@ def bench_nested(args, torch, pdk, W, dev):
                                                    / 1e9, 2)},
             "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                         "traffic": None,
+                         "traffic": traffic_record("partial_cascade.hip",
+                                                   "nested_shared_prefix_b72"),
                          "kernel": "cascade_partial_kernel (spans + level 1 in one grid)",
                          "kernel_us": best["partials_us"], "bytes_per_launch": part_bytes},
             "partial_state_bytes": state_bytes, "unique_kv_bytes": kv,
