@@ -143,6 +143,7 @@ __device__ __forceinline__ void partial_dma_body(const PartialArgs& a, const int
   // the wave's 16 query rows as B fragments: lane -> row r16, dims 32ks + 8q4 + i
   u32x4_t qf[KS];
   const int my_row = row0 + 16 * wave + r16;
+  const bool live_wave = row0 + 16 * wave < nrows;  // uniform over the wave
   // positions this lane's row sees within the partition
   const int my_end = min(end, visible_end(a, b, min(my_row, nrows - 1) / a.G));
   {
@@ -223,6 +224,8 @@ __device__ __forceinline__ void partial_dma_body(const PartialArgs& a, const int
     if (NW > 1) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     // every wave is past tile i - 1: its stage takes tile i + NS - 1
     if (i + NS - 1 < n_tiles) fetch(i + NS - 1, next);
+    // a wave without live rows only fetches and keeps the barriers
+    if (!live_wave) return;
     const int t0 = start + i * TT;
     const uint16_t* kt = buf;
     const uint16_t* vt = buf + TT * D;
