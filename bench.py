@@ -22,6 +22,7 @@ import json
 import os
 import sys
 import time
+import types
 
 import numpy as np
 
@@ -516,6 +517,27 @@ def cascade_partial_bytes(b, plan):
     return b.unique_kv_bytes() + (members + b.batch) * q_row + tables + states, states
 
 
+def planning_with_device_table_us(torch, pdk, b, csr, params, reps=50):
+    """Host time to plan a step whose page table lives on the GPU: (a) copy
+    the page ids to the host and run the host planner, (b) device detection
+    (a kernel and a two-int-per-request readback, then the host rules)."""
+    pdk.CascadePlan.from_device(csr, b.indptr, b.kv_len, b.page_size, params)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        ix = csr.indices.cpu().numpy()
+        plan = pdk.CascadePlan(b.indptr, ix, b.kv_len, b.page_size, params)
+        del plan
+    host_us = (time.perf_counter() - t0) * 1e6 / reps
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        plan = pdk.CascadePlan.from_device(csr, b.indptr, b.kv_len, b.page_size, params)
+        del plan
+    dev_us = (time.perf_counter() - t0) * 1e6 / reps
+    return {"copy_ids_then_host_plan_us": round(host_us, 1),
+            "device_detection_plan_us": round(dev_us, 1)}
+
+
 def run_arms(args, torch, pdk, b, pool, q, dev, arms_spec, tune_base=None, bytes_arm=None):
     """Time each (name, params) arm on batch b; params None: the autotuner's
     choice for the shape bucket, starting from tune_base (tuned outside the
@@ -575,7 +597,18 @@ def bench_cascade_arms(args, torch, pdk, W, dev):
                            l1_partition_tokens=512, fuse_levels=0)),
         ("cascade_all_groups_autotuned", None)),
         tune_base=pdk.CascadeParams(enabled=1, max_groups=0), bytes_arm="cascade_all_groups")
+    p_all = pdk.CascadeParams(enabled=1, max_groups=0, l0_partition_tokens=1024,
+                              l1_partition_tokens=512)
+    planning = {"batch72": planning_with_device_table_us(
+        torch, pdk, b, pdk.DeviceCSR.from_host(b.indptr, b.indices, b.kv_len, dev), p_all)}
+    # a long-context table alone: 16 groups x 16 members sharing 16384 tokens
+    ip, ix, kl = W.shared_prefix_table(1009, groups=16, members=16, prefix_tokens=16384)
+    big = types.SimpleNamespace(indptr=ip, indices=ix, kv_len=kl, page_size=16)
+    planning["batch264_ctx17k"] = planning_with_device_table_us(
+        torch, pdk, big, pdk.DeviceCSR.from_host(ip, ix, kl, dev), p_all, reps=10)
+    planning["batch264_ctx17k"]["page_ids"] = int(ip[-1])
     return {"workload": "cascade_shared_prefix_b72", "unique_kv_bytes": b.unique_kv_bytes(),
+            "device_page_table_planning": planning,
             "partial_launch_bytes": part_bytes, "partial_state_bytes": state_bytes,
             "flat_read_bytes": b.read_kv_bytes(), "arms": arms,
             "speedup_all_groups": round(arms["flat"]["us_per_step"] /

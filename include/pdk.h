@@ -301,6 +301,34 @@ int pdk_cascade_plan_get(const pdk_cascade_plan* plan, int32_t field, const int3
  * decline receives a pdk_decline. Either pointer may be NULL. */
 int pdk_cascade_plan_stats(const pdk_cascade_plan* plan, int32_t stats[6], int32_t* decline);
 
+/* Detection with the page ids on the device [cascade-PR, "Detection reads
+ * the page table, not the refcounts"; "What I left out": detection re-runs
+ * per layer per step]. csr_dev is the device page table (indptr, indices,
+ * kv_len, batch, nnz); indptr_host / kv_len_host are host copies of its row
+ * offsets [batch+1] and lengths [batch] (O(batch): what a scheduler keeps),
+ * which must describe the device table (checked: offsets from 0 to at most nnz,
+ * ceil(len / P) pages per request). A device kernel groups the requests by
+ * first page and compares each with its group's first member; two ints per
+ * request come back (the call synchronizes `stream`) and the host applies
+ * the planner's rules, so the plan equals pdk_cascade_plan_create's for the
+ * same table, except that the views' page ids are not copied to the host
+ * (PDK_PLAN_L0_INDICES / PDK_PLAN_L1_INDICES read as empty): upload it with
+ * pdk_cascade_plan_upload_device, which gathers them from csr_dev into the
+ * workspace on `stream` (csr_dev must hold the same page ids then);
+ * pdk_cascade_plan_upload refuses such a plan. scratch_dev: device memory
+ * of pdk_cascade_device_detect_scratch_bytes(batch) bytes. One level of
+ * spans only (max_depth must be 1: nested spans compare pages past a span).
+ * Errors: PDK_ERR_ARG, PDK_ERR_SHAPE, PDK_ERR_WORKSPACE, PDK_ERR_UNSUPPORTED,
+ * PDK_ERR_HIP. */
+size_t pdk_cascade_device_detect_scratch_bytes(int32_t batch);
+int pdk_cascade_plan_create_device(const pdk_csr* csr_dev, const int32_t* indptr_host,
+                                   const int32_t* kv_len_host, int32_t page_size,
+                                   const pdk_cascade_params* params, void* scratch_dev,
+                                   size_t scratch_bytes, hipStream_t stream,
+                                   pdk_cascade_plan** plan_out);
+int pdk_cascade_plan_upload_device(pdk_cascade_plan* plan, const pdk_csr* csr_dev,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Plan memoization [cascade-PR, "What I left out, and where I was unsure":
  * detection re-runs per layer per step; a plan slot in the plan cache is the
  * follow-up]. A cache of up to `capacity` plans, least recently used out

@@ -111,6 +111,9 @@ _SIGS = {
                                   _P, _S, _P, _P, _P, _P, _P]),
     "pdk_cascade_tuned_params": (_I, [_P, _I, _P, _P, _I, _I, _P, _P]),
     "pdk_cascade_tuning_clear": (None, []),
+    "pdk_cascade_device_detect_scratch_bytes": (_S, [_I]),
+    "pdk_cascade_plan_create_device": (_I, [_P, _P, _P, _I, _P, _P, _S, _P, _P]),
+    "pdk_cascade_plan_upload_device": (_I, [_P, _P, _P, _S, _P]),
     "pdk_plan_cache_create": (_I, [_I, _P]),
     "pdk_plan_cache_free": (None, [_P]),
     "pdk_plan_cache_get": (_I, [_P, _P, _I, _P, _P, _P, _P]),
@@ -431,6 +434,32 @@ class CascadePlan:
         self.workspace = None
 
     @classmethod
+    def from_device(cls, csr: "DeviceCSR", indptr_host, kv_len_host, page_size: int,
+                    params: CascadeParams, stream=None):
+        """Plan a device page table: detection runs on the GPU, the host
+        reads back two ints per request and keeps only the row offsets and
+        lengths it was given; page ids are gathered on the device at upload."""
+        ip = np.ascontiguousarray(indptr_host, dtype=np.int32)
+        kl = np.ascontiguousarray(kv_len_host, dtype=np.int32)
+        B = int(kl.size)
+        need = int(lib().pdk_cascade_device_detect_scratch_bytes(B))
+        scratch = torch.empty(max(need, 256), dtype=torch.uint8, device=csr.indptr.device)
+        cs, p = csr.struct(), params.struct()
+        h = ctypes.c_void_p()
+        _check(lib().pdk_cascade_plan_create_device(ctypes.byref(cs), ip.ctypes.data,
+                                                    kl.ctypes.data, int(page_size),
+                                                    ctypes.byref(p), _ptr(scratch),
+                                                    int(scratch.numel()), _stream(stream),
+                                                    ctypes.byref(h)))
+        self = cls.__new__(cls)
+        self._h = h
+        self._owner = None
+        self.params = params
+        self.workspace = None
+        self._csr_dev = csr
+        return self
+
+    @classmethod
     def _borrowed(cls, handle, params, owner):
         """A plan owned by a PlanCache (not freed by this object)."""
         self = cls.__new__(cls)
@@ -470,8 +499,14 @@ class CascadePlan:
         need = self.workspace_bytes(num_q_heads, head_dim_v)
         if workspace is None:
             workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
-        _check(lib().pdk_cascade_plan_upload(self._h, _ptr(workspace), int(workspace.numel()),
-                                             _stream(stream)))
+        if getattr(self, "_csr_dev", None) is not None:
+            cs = self._csr_dev.struct()
+            _check(lib().pdk_cascade_plan_upload_device(self._h, ctypes.byref(cs),
+                                                        _ptr(workspace), int(workspace.numel()),
+                                                        _stream(stream)))
+        else:
+            _check(lib().pdk_cascade_plan_upload(self._h, _ptr(workspace),
+                                                 int(workspace.numel()), _stream(stream)))
         self.workspace = workspace
         return workspace
 

@@ -103,9 +103,13 @@ struct pdk_cascade_plan {
   struct {
     size_t l0_indptr, l0_indices, l0_len, l0_parts, group_indptr, members, member_rows;
     size_t l1_indptr, l1_indices, l1_len, l1_parts, l1_rows, fused;
-    size_t l0_work, l1_work;
+    size_t l0_work, l1_work, segs;
   } off{};
   const void* uploaded_to = nullptr;
+  // page ids of the views live on the device: gathered at upload from these
+  // (source offset in the device page ids, workspace int offset, count)
+  bool device_views = false;
+  int32_t n_segs = 0;
 };
 
 extern "C" {
@@ -122,13 +126,11 @@ void pdk_cascade_params_default(pdk_cascade_params* p) {
   p->max_depth = 1;
 }
 
-int pdk_cascade_plan_create(const pdk_csr* csr, int32_t P, const pdk_cascade_params* params,
-                            pdk_cascade_plan** plan_out) {
-  if (!plan_out || !params) return fail(PDK_ERR_ARG, "NULL plan_out/params");
-  *plan_out = nullptr;
-  int st = pdk_validate_csr(csr, P, 0x7FFFFFFF);
-  if (st) return st;
-  const pdk_cascade_params& pr = *params;
+}  // extern "C"
+
+namespace {
+
+int check_params(const pdk_cascade_params& pr, int32_t P) {
   if (pr.min_shared_pages < 1 || pr.min_members < 2 || pr.max_groups < 0)
     return fail(PDK_ERR_ARG, "thresholds: min_shared_pages >= 1, min_members >= 2, max_groups >= 0");
   if (pr.l0_partition_tokens <= 0 || pr.l0_partition_tokens % P ||
@@ -137,45 +139,45 @@ int pdk_cascade_plan_create(const pdk_csr* csr, int32_t P, const pdk_cascade_par
   if (pr.fuse_levels != 0 && pr.fuse_levels != 1)
     return fail(PDK_ERR_ARG, "fuse_levels must be 0 or 1");
   if (pr.max_depth < 1) return fail(PDK_ERR_ARG, "max_depth %d < 1", pr.max_depth);
+  return PDK_OK;
+}
 
-  const int B = csr->batch;
-  const int32_t* indptr = csr->indptr;
-  const int32_t* idx = csr->indices;
-  const int32_t* len = csr->kv_len;
+}  // namespace
+
+// The plan from the detection result. leader[b]: the first request (in batch
+// order) whose range starts on the same page as b's, or -1 when b has no
+// page or no token; common[b]: the number of leading page ids b shares with
+// its leader, position by position (a leader's own page count for itself).
+// idx: the host page ids, or nullptr when they live only on the device: the
+// views' page ids are then gathered there at upload (segments recorded here)
+// and nested spans, which compare pages past a span, are not available.
+static int upload_blob(pdk_cascade_plan* plan, void* ws, size_t ws_bytes, hipStream_t stream);
+
+static int build_plan(int B, int32_t P, const pdk_cascade_params& pr, const int32_t* indptr,
+               const int32_t* len, const int32_t* idx, const std::vector<int32_t>& leader,
+               const std::vector<int32_t>& common, pdk_cascade_plan** plan_out) {
   auto plan = new pdk_cascade_plan();
   plan->batch = B;
   plan->page_size = P;
   plan->params = pr;
+  plan->device_views = idx == nullptr;
 
   std::vector<Candidate> chosen;
   if (pr.enabled != 1) {
     plan->decline = PDK_DECLINE_DISABLED;
   } else {
-    // group candidates by first page, members in batch order
-    std::map<int32_t, std::vector<int32_t>> by_first;
-    std::vector<int32_t> order;  // first ids in order of first appearance
-    for (int b = 0; b < B; ++b) {
-      if (indptr[b + 1] - indptr[b] < 1 || len[b] < 1) continue;
-      auto it = by_first.find(idx[indptr[b]]);
-      if (it == by_first.end()) order.push_back(idx[indptr[b]]);
-      by_first[idx[indptr[b]]].push_back(b);
-    }
+    // groups: requests with the same leader (the first member), in order of
+    // their leaders; a group's common prefix is the smallest of its members'
+    // prefixes shared with the leader
+    std::map<int32_t, std::vector<int32_t>> by_leader;
+    for (int b = 0; b < B; ++b)
+      if (leader[b] >= 0) by_leader[leader[b]].push_back(b);
     std::vector<Candidate> cands;
-    for (int32_t first : order) {
-      const auto& mem = by_first[first];
+    for (const auto& kv : by_leader) {
+      const auto& mem = kv.second;
       if (mem.size() < 2) continue;
-      // longest common page prefix, position by position
-      int32_t lcp = 0;
-      for (;;) {
-        bool ok = true;
-        for (int32_t b : mem)
-          if (lcp >= indptr[b + 1] - indptr[b] || idx[indptr[b] + lcp] != idx[indptr[mem[0]] + lcp]) {
-            ok = false;
-            break;
-          }
-        if (!ok) break;
-        ++lcp;
-      }
+      int32_t lcp = common[mem[0]];
+      for (int32_t b : mem) lcp = std::min(lcp, common[b]);
       // every shared page full
       int32_t span = lcp;
       for (int32_t b : mem) span = std::min(span, len[b] / P);
@@ -221,7 +223,7 @@ int pdk_cascade_plan_create(const pdk_csr* csr, int32_t P, const pdk_cascade_par
   for (const auto& c : chosen) nodes.push_back({c.members, 0, c.span, 0, -1});
   {
     size_t lo = 0, hi = nodes.size();
-    for (int depth = 1; depth < pr.max_depth && lo < hi; ++depth) {
+    for (int depth = 1; depth < pr.max_depth && idx && lo < hi; ++depth) {
       std::vector<SpanNode> next;
       for (size_t i = lo; i < hi; ++i) {
         const int32_t e = nodes[i].start + nodes[i].span;
@@ -261,6 +263,10 @@ int pdk_cascade_plan_create(const pdk_csr* csr, int32_t P, const pdk_cascade_par
 
   auto& F = plan->f;
   const int K = (int)nodes.size();
+  // view page ids (zeros where the device fills them from the segments)
+  struct Seg { int32_t src, dst, count; };
+  std::vector<int32_t> l0_idx, l1_idx;
+  std::vector<Seg> l0_segs, l1_segs;
   plan->n_groups = K;
   std::vector<int32_t> group_of(B, -1), rank(B, -1), private_start(B, 0), n_spans(B, 0);
   F[PDK_PLAN_GROUP_INDPTR].push_back(0);
@@ -283,8 +289,13 @@ int pdk_cascade_plan_create(const pdk_csr* csr, int32_t P, const pdk_cascade_par
     F[PDK_PLAN_SPAN_START].push_back(c.start);
     F[PDK_PLAN_SPAN_PARENT].push_back(c.parent);
     const int b0 = c.members[0];
-    for (int i = 0; i < c.span; ++i) F[PDK_PLAN_L0_INDICES].push_back(idx[indptr[b0] + c.start + i]);
-    F[PDK_PLAN_L0_INDPTR].push_back((int32_t)F[PDK_PLAN_L0_INDICES].size());
+    if (idx) {
+      for (int i = 0; i < c.span; ++i) l0_idx.push_back(idx[indptr[b0] + c.start + i]);
+    } else {
+      l0_segs.push_back({indptr[b0] + c.start, (int32_t)l0_idx.size(), c.span});
+      l0_idx.resize(l0_idx.size() + c.span, 0);
+    }
+    F[PDK_PLAN_L0_INDPTR].push_back((int32_t)l0_idx.size());
     F[PDK_PLAN_L0_LEN].push_back(c.span * P);
     plan->max_members = std::max(plan->max_members, (int32_t)c.members.size());
   }
@@ -292,13 +303,23 @@ int pdk_cascade_plan_create(const pdk_csr* csr, int32_t P, const pdk_cascade_par
   F[PDK_PLAN_MERGE_INDPTR].push_back(0);
   for (int b = 0; b < B; ++b) {
     const int s = private_start[b];
-    for (int i = indptr[b] + s; i < indptr[b + 1]; ++i) F[PDK_PLAN_L1_INDICES].push_back(idx[i]);
-    F[PDK_PLAN_L1_INDPTR].push_back((int32_t)F[PDK_PLAN_L1_INDICES].size());
+    if (idx) {
+      for (int i = indptr[b] + s; i < indptr[b + 1]; ++i) l1_idx.push_back(idx[i]);
+    } else {
+      const int n = indptr[b + 1] - indptr[b] - s;
+      l1_segs.push_back({indptr[b] + s, (int32_t)l1_idx.size(), n});
+      l1_idx.resize(l1_idx.size() + n, 0);
+    }
+    F[PDK_PLAN_L1_INDPTR].push_back((int32_t)l1_idx.size());
     F[PDK_PLAN_L1_LEN].push_back(len[b] - s * P);
     F[PDK_PLAN_MERGE_INDPTR].push_back(F[PDK_PLAN_MERGE_INDPTR].back() + n_spans[b] + 1);
   }
   F[PDK_PLAN_GROUP_OF] = group_of;
   F[PDK_PLAN_MEMBER_RANK] = rank;
+  if (idx) {
+    F[PDK_PLAN_L0_INDICES] = l0_idx;
+    F[PDK_PLAN_L1_INDICES] = l1_idx;
+  }
 
   // partitions of both levels and the fused row layout
   const int S0 = pr.l0_partition_tokens, S1 = pr.l1_partition_tokens;
@@ -355,14 +376,14 @@ int pdk_cascade_plan_create(const pdk_csr* csr, int32_t P, const pdk_cascade_par
   // device blob (uploaded to the head of the workspace)
   auto& bl = plan->blob;
   plan->off.l0_indptr = bl.add(F[PDK_PLAN_L0_INDPTR]);
-  plan->off.l0_indices = bl.add(F[PDK_PLAN_L0_INDICES]);
+  plan->off.l0_indices = bl.add(l0_idx);
   plan->off.l0_len = bl.add(F[PDK_PLAN_L0_LEN]);
   plan->off.l0_parts = bl.add(plan->l0_part_indptr);
   plan->off.group_indptr = bl.add(F[PDK_PLAN_GROUP_INDPTR]);
   plan->off.members = bl.add(F[PDK_PLAN_MEMBERS]);
   plan->off.member_rows = bl.add(plan->member_row_base);
   plan->off.l1_indptr = bl.add(F[PDK_PLAN_L1_INDPTR]);
-  plan->off.l1_indices = bl.add(F[PDK_PLAN_L1_INDICES]);
+  plan->off.l1_indices = bl.add(l1_idx);
   plan->off.l1_len = bl.add(F[PDK_PLAN_L1_LEN]);
   plan->off.l1_parts = bl.add(plan->l1_part_indptr);
   plan->off.l1_rows = bl.add(plan->l1_row_base);
@@ -371,8 +392,111 @@ int pdk_cascade_plan_create(const pdk_csr* csr, int32_t P, const pdk_cascade_par
   // workgroups in order, so the short tail partitions fill the last gaps
   plan->off.l0_work = bl.add(longest_first(plan->l0_part_indptr, F[PDK_PLAN_L0_LEN], S0));
   plan->off.l1_work = bl.add(longest_first(plan->l1_part_indptr, F[PDK_PLAN_L1_LEN], S1));
+  if (!idx) {
+    std::vector<int32_t> segs;
+    for (const auto& g : l0_segs)
+      segs.insert(segs.end(), {g.src, (int32_t)plan->off.l0_indices + g.dst, g.count});
+    for (const auto& g : l1_segs)
+      segs.insert(segs.end(), {g.src, (int32_t)plan->off.l1_indices + g.dst, g.count});
+    plan->n_segs = (int32_t)(segs.size() / 3);
+    plan->off.segs = bl.add(segs);
+  }
   *plan_out = plan;
   return PDK_OK;
+}
+
+extern "C" {
+
+int pdk_cascade_plan_create(const pdk_csr* csr, int32_t P, const pdk_cascade_params* params,
+                            pdk_cascade_plan** plan_out) {
+  if (!plan_out || !params) return fail(PDK_ERR_ARG, "NULL plan_out/params");
+  *plan_out = nullptr;
+  int st = pdk_validate_csr(csr, P, 0x7FFFFFFF);
+  if (st) return st;
+  if ((st = check_params(*params, P))) return st;
+  const int B = csr->batch;
+  const int32_t* indptr = csr->indptr;
+  const int32_t* idx = csr->indices;
+  const int32_t* len = csr->kv_len;
+  // detection on the host: leaders by first page, prefixes shared with them
+  std::vector<int32_t> leader(B, -1), common(B, 0);
+  std::map<int32_t, int32_t> first_of;
+  for (int b = 0; b < B; ++b) {
+    const int np = indptr[b + 1] - indptr[b];
+    if (np < 1 || len[b] < 1) continue;
+    const int32_t L = first_of.emplace(idx[indptr[b]], b).first->second;
+    leader[b] = L;
+    const int n = std::min(np, indptr[L + 1] - indptr[L]);
+    int c = 0;
+    while (c < n && idx[indptr[b] + c] == idx[indptr[L] + c]) ++c;
+    common[b] = c;
+  }
+  return build_plan(B, P, *params, indptr, len, idx, leader, common, plan_out);
+}
+
+size_t pdk_cascade_device_detect_scratch_bytes(int32_t batch) {
+  if (batch < 0) return 0;
+  return align256(2 * (size_t)std::max(batch, 1) * sizeof(int32_t));
+}
+
+int pdk_cascade_plan_create_device(const pdk_csr* csr_dev, const int32_t* indptr_host,
+                                   const int32_t* kv_len_host, int32_t P,
+                                   const pdk_cascade_params* params, void* scratch,
+                                   size_t scratch_bytes, hipStream_t stream,
+                                   pdk_cascade_plan** plan_out) {
+  if (!plan_out || !params || !csr_dev || !indptr_host || (csr_dev->batch > 0 && !kv_len_host))
+    return fail(PDK_ERR_ARG, "NULL argument");
+  *plan_out = nullptr;
+  const int B = csr_dev->batch;
+  if (B < 0 || csr_dev->nnz < 0) return fail(PDK_ERR_ARG, "batch %d, nnz %d", B, csr_dev->nnz);
+  if (P <= 0) return fail(PDK_ERR_ARG, "page_size %d", P);
+  int st = check_params(*params, P);
+  if (st) return st;
+  if (params->max_depth != 1)
+    return fail(PDK_ERR_UNSUPPORTED, "device detection finds one level of spans (max_depth 1)");
+  // the host copies of the row offsets and lengths must describe the device
+  // table: every page-id read of the kernels stays inside [0, nnz)
+  if (indptr_host[0] != 0 || indptr_host[B] > csr_dev->nnz)
+    return fail(PDK_ERR_SHAPE, "indptr[0] = %d, indptr[batch] = %d, nnz = %d", indptr_host[0],
+                indptr_host[B], csr_dev->nnz);
+  for (int b = 0; b < B; ++b) {
+    const int n = indptr_host[b + 1] - indptr_host[b];
+    if (n < 0 || kv_len_host[b] < 0 || n != ceil_div(kv_len_host[b], P))
+      return fail(PDK_ERR_SHAPE, "request %d: %d pages for %d tokens at page size %d", b, n,
+                  kv_len_host[b], P);
+  }
+  std::vector<int32_t> leader(B, -1), common(B, 0);
+  if (B > 0 && params->enabled == 1) {
+    if (!csr_dev->indptr || !csr_dev->kv_len || (csr_dev->nnz > 0 && !csr_dev->indices))
+      return fail(PDK_ERR_ARG, "NULL device page table");
+    if (!scratch || scratch_bytes < pdk_cascade_device_detect_scratch_bytes(B))
+      return fail(PDK_ERR_WORKSPACE, "detection scratch %zu bytes < %zu", scratch_bytes,
+                  pdk_cascade_device_detect_scratch_bytes(B));
+    // leader[B] then common[B], read back with one copy
+    int32_t* d_out = (int32_t*)scratch;
+    if ((st = launch_detect(csr_dev->indptr, csr_dev->indices, csr_dev->kv_len, B, d_out,
+                            d_out + B, stream)))
+      return st;
+    std::vector<int32_t> both(2 * (size_t)B);
+    hipError_t e = hipMemcpyAsync(both.data(), d_out, both.size() * sizeof(int32_t),
+                                  hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return fail(PDK_ERR_HIP, "detection readback: %s", hipGetErrorString(e));
+    leader.assign(both.begin(), both.begin() + B);
+    common.assign(both.begin() + B, both.end());
+  }
+  return build_plan(B, P, *params, indptr_host, kv_len_host, nullptr, leader, common, plan_out);
+}
+
+int pdk_cascade_plan_upload_device(pdk_cascade_plan* plan, const pdk_csr* csr_dev, void* ws,
+                                   size_t ws_bytes, hipStream_t stream) {
+  if (!plan || !csr_dev) return fail(PDK_ERR_ARG, "NULL plan/csr");
+  int st = upload_blob(plan, ws, ws_bytes, stream);
+  if (st || !plan->device_views || plan->n_segs == 0) return st;
+  if (plan->batch != csr_dev->batch || !csr_dev->indices)
+    return fail(PDK_ERR_ARG, "device page table does not match the plan");
+  const int32_t* segs = (const int32_t*)ws + plan->off.segs;
+  return launch_gather_pages(csr_dev->indices, segs, plan->n_segs, (int32_t*)ws, stream);
 }
 
 void pdk_cascade_plan_free(pdk_cascade_plan* plan) { delete plan; }
@@ -402,7 +526,9 @@ size_t pdk_cascade_workspace_bytes(const pdk_cascade_plan* plan, int32_t Hq, int
   return cascade_state_offset(plan) + align256(rows * Dv * sizeof(float)) + rows * sizeof(float);
 }
 
-int pdk_cascade_plan_upload(pdk_cascade_plan* plan, void* ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+static int upload_blob(pdk_cascade_plan* plan, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!plan || !ws) return fail(PDK_ERR_ARG, "NULL plan/workspace");
   if (ws_bytes < plan->blob.bytes())
     return fail(PDK_ERR_WORKSPACE, "workspace %zu bytes < plan %zu", ws_bytes, plan->blob.bytes());
@@ -413,6 +539,14 @@ int pdk_cascade_plan_upload(pdk_cascade_plan* plan, void* ws, size_t ws_bytes, h
   }
   plan->uploaded_to = ws;
   return PDK_OK;
+}
+
+extern "C" {
+
+int pdk_cascade_plan_upload(pdk_cascade_plan* plan, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (plan && plan->device_views)
+    return fail(PDK_ERR_ARG, "plan's page ids live on the device: use pdk_cascade_plan_upload_device");
+  return upload_blob(plan, ws, ws_bytes, stream);
 }
 
 int pdk_run_cascade_partials(const pdk_cascade_plan* plan, const pdk_kv_pool* pool,

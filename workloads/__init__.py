@@ -341,6 +341,34 @@ def mla_decode_share(seed: int = 1005, batch: int = 32, heads: int = 128,
     return MlaShare(prefix=prefix, suffix=suffix, chunk_tokens=chunk_tokens)
 
 
+def shared_prefix_table(seed: int, groups: int, members: int, prefix_tokens: int,
+                        suffix_min: int = 64, suffix_max: int = 1024, extra: int = 8,
+                        extra_tokens: int = 2048, page_size: int = 16):
+    """The page table alone (host indptr, indices, kv_len) of a shared-prefix
+    batch shaped like cascade_shared_prefix, without a KV pool: for planning
+    measurements on tables too large to fill with data. Pool rows are a
+    seeded permutation of the logical pages."""
+    rng = np.random.default_rng(seed)
+    P = page_size
+    seqs, nxt = [], 0
+    for g in range(groups):
+        pref = list(range(nxt, nxt + prefix_tokens // P))
+        nxt += len(pref)
+        for _ in range(members):
+            suf = int(rng.integers(suffix_min, suffix_max + 1))
+            npg = _pages(suf, P)
+            seqs.append((pref + list(range(nxt, nxt + npg)), prefix_tokens + suf))
+            nxt += npg
+    for _ in range(extra):
+        npg = _pages(extra_tokens, P)
+        seqs.append((list(range(nxt, nxt + npg)), extra_tokens))
+        nxt += npg
+    order = rng.permutation(len(seqs))
+    rows = rng.permutation(nxt)
+    lists = [[int(rows[p]) for p in seqs[i][0]] for i in order]
+    return csr_from_page_lists(lists, [seqs[i][1] for i in order])
+
+
 def nested_shared_prefix(seed: int = 1008, tenants: int = 4, members: int = 16,
                          system_tokens: int = 2048, tenant_tokens: int = 2048,
                          suffix_min: int = 64, suffix_max: int = 1024, extra: int = 8,
