@@ -167,11 +167,12 @@ int pdk_cascade_autotune(const pdk_csr* csr_host, int32_t page_size,
     }
   }
   const size_t n16 = flush_buffer ? flush_bytes / 16 : 0;
-  hipEvent_t ev[2];
-  if (hipEventCreate(&ev[0]) != hipSuccess || hipEventCreate(&ev[1]) != hipSuccess)
+  hipEvent_t ev[2] = {nullptr, nullptr};
+  if (hipEventCreate(&ev[0]) != hipSuccess || hipEventCreate(&ev[1]) != hipSuccess) {
+    if (ev[0]) (void)hipEventDestroy(ev[0]);
     return fail(PDK_ERR_HIP, "event create failed");
+  }
   TuneResult best{0, 0, INFINITY};
-  const int Dv = pool->head_dim_v;
   for (int i = 0; i < n_l0 && !st; ++i)
     for (int j = 0; j < n_l1 && !st; ++j) {
       pdk_cascade_params p = *params;
@@ -187,26 +188,28 @@ int pdk_cascade_autotune(const pdk_csr* csr_host, int32_t page_size,
                              (uint4*)flush_buffer, n16, 0x9E3779B9u);
           if (hipGetLastError() != hipSuccess) { st = fail(PDK_ERR_HIP, "flush launch"); break; }
         }
-        hipEventRecord(ev[0], stream);
+        if (hipEventRecord(ev[0], stream) != hipSuccess) { st = fail(PDK_ERR_HIP, "event record"); break; }
         st = pdk_run_cascade_decode(plan, pool, q, q_dtype, num_q_heads, sm_scale, out, lse_out,
                                     workspace, workspace_bytes, stream);
-        hipEventRecord(ev[1], stream);
         if (st) break;
-        if (hipEventSynchronize(ev[1]) != hipSuccess) { st = fail(PDK_ERR_HIP, "event sync"); break; }
         float ms = 0.f;
-        hipEventElapsedTime(&ms, ev[0], ev[1]);
+        if (hipEventRecord(ev[1], stream) != hipSuccess || hipEventSynchronize(ev[1]) != hipSuccess ||
+            hipEventElapsedTime(&ms, ev[0], ev[1]) != hipSuccess) {
+          st = fail(PDK_ERR_HIP, "event timing");
+          break;
+        }
         if (r >= 0) total_ms += ms;
       }
       // the upload read the plan's host arrays: done once the stream is idle
-      hipStreamSynchronize(stream);
+      if (hipStreamSynchronize(stream) != hipSuccess && !st) st = fail(PDK_ERR_HIP, "stream sync");
       pdk_cascade_plan_free(plan);
       if (st) break;
       const float us = (float)(1000.0 * total_ms / reps);
       if (times_us) times_us[i * n_l1 + j] = us;
       if (us < best.us) best = TuneResult{p.l0_partition_tokens, p.l1_partition_tokens, us};
     }
-  hipEventDestroy(ev[0]);
-  hipEventDestroy(ev[1]);
+  (void)hipEventDestroy(ev[0]);
+  (void)hipEventDestroy(ev[1]);
   if (st) return st;
   {
     std::lock_guard<std::mutex> lock(g_tune_mu);

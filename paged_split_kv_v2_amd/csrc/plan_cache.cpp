@@ -54,7 +54,7 @@ struct Entry {
 struct pdk_plan_cache {
   int capacity = 0;
   std::list<Entry> lru;  // most recently used first
-  std::mutex mu;
+  mutable std::mutex mu;
   int64_t next_id = 1;
   int64_t lookups = 0, hits = 0, builds = 0, evictions = 0;
 };
@@ -121,13 +121,12 @@ int pdk_plan_cache_get(pdk_plan_cache* cache, const pdk_csr* csr, int32_t P,
 
 int pdk_plan_cache_stats(const pdk_plan_cache* cache, int64_t stats[5]) {
   if (!cache || !stats) return fail(PDK_ERR_ARG, "NULL argument");
-  auto* c = const_cast<pdk_plan_cache*>(cache);
-  std::lock_guard<std::mutex> lock(c->mu);
-  stats[0] = c->lookups;
-  stats[1] = c->hits;
-  stats[2] = c->builds;
-  stats[3] = c->evictions;
-  stats[4] = (int64_t)c->lru.size();
+  std::lock_guard<std::mutex> lock(cache->mu);
+  stats[0] = cache->lookups;
+  stats[1] = cache->hits;
+  stats[2] = cache->builds;
+  stats[3] = cache->evictions;
+  stats[4] = (int64_t)cache->lru.size();
   return PDK_OK;
 }
 
