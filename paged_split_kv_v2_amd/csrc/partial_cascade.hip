@@ -22,14 +22,20 @@ namespace pdk {
 namespace {
 
 constexpr int kL0Waves = 4;  // level-0 body: 4 waves x 16 stacked query rows
+constexpr int kL0Stages = 2;  // level-0 LDS ring: two 32-token stages
 static_assert(64 * kL0Waves == kThreads, "both bodies run on 256-thread workgroups");
 
-__global__ __launch_bounds__(256) void cascade_partial_kernel(const PartialArgs a0,
-                                                              const PartialArgs a1,
-                                                              const int blocks0) {
+// Three workgroups per compute unit: the level-1 body alone fits three (156
+// registers), and with a two-stage ring the level-0 body keeps its
+// accumulators in the same budget (no accumulator registers), 47 KB of LDS
+// each. A deeper ring would hold more of level 0 in flight but costs the
+// third workgroup, which level 1 - most of the bytes - needs more (measured
+// on the batch-72 shared-prefix step: 57 against 64 us).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void cascade_partial_kernel(const PartialArgs a0, const PartialArgs a1, const int blocks0) {
   const int bid = blockIdx.x;
   if (bid < blocks0)
-    partial_dma_body<128, 32, 4, kL0Waves, true>(a0, bid);
+    partial_dma_body<128, 32, kL0Stages, kL0Waves, true>(a0, bid);
   else
     partial_valu_body<KV_BF16, PDK_BF16, 128, 4, true, false>(a1, bid - blocks0);
 }
@@ -41,8 +47,8 @@ __global__ __launch_bounds__(256) void cascade_partial_kernel(const PartialArgs 
 // (more than 4 stacked rows per KV head, as for its own launch) and level 1
 // on the vector body with a row tile of 4 query rows (3 or 4 rows per KV
 // head). Any other shape is left to the separate launches (*handled false).
-// (A row tile of 8 would need 88 KB of LDS per workgroup, one workgroup per
-// compute unit.)
+// (A row tile of 8 would need more registers than three workgroups per
+// compute unit leave.)
 int launch_cascade_partials(const PartialArgs& a0, const PartialArgs& a1, hipStream_t stream,
                             bool* handled) {
   *handled = false;

@@ -9,8 +9,15 @@ namespace pdk {
 
 namespace {
 
+// Four workgroups per compute unit: with a two-stage ring the body fits 128
+// registers (accumulators included) and 35 KB of LDS. Measured on the 4-token
+// Llama-3-8B step (16 rows per KV head): 235 us here, 273 us with a
+// four-stage ring at two workgroups per compute unit, 238 us with three
+// stages at three; occupancy hides the per-tile barrier and products better
+// than a deeper ring hides memory latency.
 template <int D, int TT, int NS, int NW, bool SPLIT>
-__global__ __launch_bounds__(64 * NW) void partial_dma_kernel(const PartialArgs a) {
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void partial_dma_kernel(const PartialArgs a) {
   partial_dma_body<D, TT, NS, NW, SPLIT>(a, blockIdx.x);
 }
 
@@ -22,18 +29,19 @@ typedef void (*DmaFn)(const PartialArgs);
 // a power of two >= 4 tokens, more than 4 query rows per KV head (stacked
 // level-0 rows, multi-token steps, query groups of 8 or 16): this path takes
 // the launch (*handled) with 4 waves (64 rows per row tile). With up to 4
-// rows per KV head the vector kernel streams faster (three workgroups of 64
-// KB in flight per CU, against two of 48 KB here); from 8 rows on it spends
-// more on its register-held products than the LDS ring loses (measured on a
-// 64-request step of 8 and 16 rows per KV head: 277 and 283 us here against
-// 357 and 1046 us on the vector kernel).
+// rows per KV head the vector kernel streams faster (64 KB of rows in flight
+// per workgroup in registers); from 8 rows on it spends more on its
+// register-held products than the LDS ring loses (measured on a 64-request
+// step of 8 and 16 rows per KV head, before the ring took two stages at four
+// workgroups per compute unit: 277 and 283 us here against 357 and 1046 us on
+// the vector kernel).
 int launch_partial_dma(const PartialArgs& a, hipStream_t stream, bool* handled) {
   *handled = false;
   if (a.q_dtype != PDK_BF16 || a.kv_dtype != PDK_BF16 || a.v == nullptr || a.Dk != 128 ||
       a.Dv != 128 || a.p_shift < 2 || a.max_rows <= 4)
     return PDK_OK;
   const int nw = 4;
-  DmaFn fn = partial_dma_kernel<128, 32, 4, 4, true>;
+  DmaFn fn = partial_dma_kernel<128, 32, 2, 4, true>;
   if (a.S / a.P + 1 > kMaxPagesD)
     return fail(PDK_ERR_UNSUPPORTED, "partition of %d tokens spans more than %d pages", a.S,
                 kMaxPagesD - 1);
