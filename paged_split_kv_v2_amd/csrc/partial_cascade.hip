@@ -64,8 +64,8 @@ int launch_cascade_partials(const PartialArgs& a0, const PartialArgs& a1, hipStr
   int gm = 1;
   while (gm < a1.max_rows && gm < valu_max_rows(a1.Dk)) gm <<= 1;
   if (gm != 4) return PDK_OK;
-  const long long blocks0 =
-      (long long)a0.num_parts * a0.Hkv * ((a0.max_rows + 16 * kL0Waves - 1) / (16 * kL0Waves));
+  const long long blocks0 = xcd_grid_blocks(
+      (long long)a0.num_parts * a0.Hkv, (a0.max_rows + 16 * kL0Waves - 1) / (16 * kL0Waves));
   const long long blocks1 = (long long)a1.num_parts * a1.Hkv;  // one row tile
   if (blocks0 == 0 || blocks1 == 0) return PDK_OK;
   if (blocks0 + blocks1 > 0x7FFFFFFFLL)

@@ -47,7 +47,7 @@ int launch_partial_dma(const PartialArgs& a, hipStream_t stream, bool* handled) 
                 kMaxPagesD - 1);
   *handled = true;
   const int n_rt = (a.max_rows + 16 * nw - 1) / (16 * nw);
-  const long long blocks = (long long)a.num_parts * a.Hkv * n_rt;
+  const long long blocks = xcd_grid_blocks((long long)a.num_parts * a.Hkv, n_rt);
   if (blocks == 0) return PDK_OK;
   if (blocks > 0x7FFFFFFFLL) return fail(PDK_ERR_SHAPE, "grid too large (%lld)", blocks);
   hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(64 * nw), 0, stream, a);

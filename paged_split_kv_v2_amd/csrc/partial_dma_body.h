@@ -88,11 +88,11 @@ __device__ __forceinline__ void partial_dma_body(const PartialArgs& a, const int
   __shared__ int sm_pid[kMaxPagesD];
 
   const int n_rt = (a.max_rows + 16 * NW - 1) / (16 * NW);
-  int bid = block;
-  const int rt = bid % n_rt;
-  bid /= n_rt;
-  const int h = bid % a.Hkv;
-  const int r = bid / a.Hkv;
+  int unit, rt;
+  xcd_unit_tile(block, n_rt, unit, rt);
+  if (unit >= a.num_parts * a.Hkv) return;  // grid padding (uniform)
+  const int h = unit % a.Hkv;
+  const int r = unit / a.Hkv;
   const int tid = threadIdx.x;
 
   int b = 0, p;

@@ -96,13 +96,12 @@ void partial_latent_kernel(const PartialArgs a) {
   __shared__ __align__(16) u32x4_t sraw[ITEMS];         // fetched rows, item order
   __shared__ int sm_pid[kMaxPagesL];
 
-  // block -> (unit = partition * Hkv + kv head, row tile): the row tiles of a
-  // unit are adjacent blocks
+  // block -> (unit = partition * Hkv + kv head, row tile), a unit's row
+  // tiles on one XCD
   const int n_tiles = (a.max_rows + kRows - 1) / kRows;
-  const int bid = blockIdx.x;
-  const int unit = bid / n_tiles;
-  const int tile = bid - unit * n_tiles;
-  if (unit >= a.num_parts * a.Hkv) return;  // uniform; the grid has no padding
+  int unit, tile;
+  xcd_unit_tile(blockIdx.x, n_tiles, unit, tile);
+  if (unit >= a.num_parts * a.Hkv) return;  // grid padding (uniform)
   const int h = unit % a.Hkv;
   const int r = unit / a.Hkv;
   const int tid = threadIdx.x;
@@ -426,7 +425,7 @@ int launch_partial_latent(const PartialArgs& a, hipStream_t stream, bool* handle
   *handled = true;
   const int n_tiles = (a.max_rows + kRows - 1) / kRows;
   const long long units = (long long)a.num_parts * a.Hkv;
-  const long long blocks = units * n_tiles;
+  const long long blocks = xcd_grid_blocks(units, n_tiles);
   if (blocks == 0) return PDK_OK;
   if (blocks > 0x7FFFFFFFLL) return fail(PDK_ERR_SHAPE, "grid too large (%lld)", blocks);
   hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(64 * kWaves), 0, stream, a);

@@ -93,11 +93,11 @@ __global__ __launch_bounds__(64 * NW) void partial_mfma_kernel(const PartialArgs
   __shared__ int sm_pid[kMaxPartPagesM];
 
   const int n_tiles = (a.max_rows + 16 * NW - 1) / (16 * NW);
-  int bid = blockIdx.x;
-  const int tile = bid % n_tiles;
-  bid /= n_tiles;
-  const int h = bid % a.Hkv;
-  const int r = bid / a.Hkv;
+  int unit, tile;
+  xcd_unit_tile(blockIdx.x, n_tiles, unit, tile);
+  if (unit >= a.num_parts * a.Hkv) return;  // grid padding (uniform)
+  const int h = unit % a.Hkv;
+  const int r = unit / a.Hkv;
   const int tid = threadIdx.x;
 
   int b = 0, p;
@@ -421,7 +421,7 @@ int launch_partial_mfma(const PartialArgs& a, hipStream_t stream, bool* handled)
                 kMaxPartPagesM - 1);
   *handled = true;
   const int n_tiles = (a.max_rows + 16 * nw - 1) / (16 * nw);
-  const long long blocks = (long long)a.num_parts * a.Hkv * n_tiles;
+  const long long blocks = xcd_grid_blocks((long long)a.num_parts * a.Hkv, n_tiles);
   if (blocks == 0) return PDK_OK;
   if (blocks > 0x7FFFFFFFLL) return fail(PDK_ERR_SHAPE, "grid too large (%lld)", blocks);
   hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(64 * nw), 0, stream, a);

@@ -74,7 +74,7 @@ int launch_partial_valu(const PartialArgs& a, hipStream_t stream) {
                 "no vector kernel for kv dtype %d, q dtype %d, head dim %d, %d rows", kt, qt,
                 a.Dk, gm);
   const int n_tiles = (a.max_rows + gm - 1) / gm;
-  const long long blocks = (long long)a.num_parts * a.Hkv * n_tiles;
+  const long long blocks = xcd_grid_blocks((long long)a.num_parts * a.Hkv, n_tiles);
   if (blocks == 0) return PDK_OK;
   if (blocks > 0x7FFFFFFFLL) return fail(PDK_ERR_SHAPE, "grid too large (%lld)", blocks);
   hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);

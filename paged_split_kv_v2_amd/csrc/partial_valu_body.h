@@ -118,11 +118,11 @@ __device__ __forceinline__ void partial_valu_body(const PartialArgs& a, const in
   __shared__ int sm_pid[kMaxPartPages];
 
   const int n_tiles = (a.max_rows + GM - 1) / GM;
-  int bid = block;
-  const int tile = bid % n_tiles;
-  bid /= n_tiles;
-  const int h = bid % a.Hkv;
-  const int r = bid / a.Hkv;
+  int unit, tile;
+  xcd_unit_tile(block, n_tiles, unit, tile);
+  if (unit >= a.num_parts * a.Hkv) return;  // grid padding (uniform)
+  const int h = unit % a.Hkv;
+  const int r = unit / a.Hkv;
 
   const int tid = threadIdx.x;
   int b = 0, p;

@@ -45,6 +45,27 @@ __device__ __forceinline__ size_t state_index(const PartialArgs& a, bool stacked
   return ((size_t)row * a.q_tokens + t) * a.Hq + head;
 }
 
+// Row tiles of one unit (view request partition x KV head) on one XCD. The
+// hardware hands consecutive workgroups of a grid to the eight XCDs in turn,
+// so blocks b, b + 8, b + 16, ... run on one XCD and share its L2; a unit's
+// n_rt row tiles all read the unit's pages, so they are placed 8 blocks
+// apart. Grids with several row tiles are padded to whole groups of 8 units
+// (xcd_grid_blocks); a padding block gets unit >= the unit count and exits.
+__host__ __device__ inline long long xcd_grid_blocks(long long units, int n_rt) {
+  return n_rt == 1 ? units : (units + 7) / 8 * 8 * n_rt;
+}
+
+__device__ __forceinline__ void xcd_unit_tile(int block, int n_rt, int& unit, int& tile) {
+  if (n_rt == 1) {
+    unit = block;
+    tile = 0;
+    return;
+  }
+  const int group = block / (8 * n_rt), r = block - group * 8 * n_rt;
+  unit = group * 8 + (r & 7);
+  tile = r >> 3;
+}
+
 // Exclusive end of the positions row group n sees (INT_MAX: the whole range).
 __device__ __forceinline__ int visible_end(const PartialArgs& a, int b, int n) {
   if (!a.causal) return INT_MAX;
