@@ -136,6 +136,25 @@ def test_nested_sharing(gpu, depth):
     assert lse_err(lse, fl.cpu().numpy()) <= 1e-5
 
 
+def test_nested_full_workload_sampled(gpu):
+    """The benchmark's nested workload at full size (batch 72, 2048-token
+    system prompt, 4 tenant sub-prefixes of 2048 tokens) with nested spans:
+    sampled requests against the oracle, all of it against the flat launch."""
+    b = W.nested_shared_prefix()
+    pool, csr, q = to_device(b)
+    params = gpu.CascadeParams(enabled=1, max_groups=0, max_depth=2, l0_partition_tokens=1024,
+                               l1_partition_tokens=512)
+    out, lse, plan = cascade(gpu, b, params, pool, q)
+    assert len(plan.field("span_pages")) == 5
+    fo, fl, _ = flat_decode(b, pool, csr, q, 512)
+    assert rel_err(out, fo.cpu().numpy()) <= 1e-5
+    assert lse_err(lse, fl.cpu().numpy()) <= 1e-5
+    reqs = [0, 9, 40, 71]
+    ro, rl = oatt.decode_attention(b, requests=reqs)
+    assert_close(out[reqs], ro[reqs], TOL["bf16"], "nested out")
+    assert_lse(lse[reqs], rl[reqs], "nested lse")
+
+
 def test_declined_plan_runs_flat(gpu):
     b = W.llama3_8b_flat(seed=2005, batch=5, min_len=100, max_len=900)
     pool, csr, q = to_device(b)

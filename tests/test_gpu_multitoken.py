@@ -136,3 +136,22 @@ def test_multi_token_repeat_is_deterministic(gpu):
     second = mt_partials(gpu, b, True, 64)
     for x, y in zip(first[:4], second[:4]):
         assert np.array_equal(x, y)
+
+
+def test_full_size_four_token_step_sampled(gpu):
+    """The benchmark's 4-token step at its full size (batch 64, contexts
+    U[1024, 8192], 512-token partitions, the launch bench.py times): sampled
+    requests against the oracle, every output finite."""
+    b = W.with_query_tokens(W.llama3_8b_flat(), 4, 1006)
+    pool, csr, q = to_device(b)
+    S = b.partition_tokens
+    pind = gpu.partition_indptr(b.kv_len, S)
+    out, lse = gpu.multi_token_flat(pool, csr, q, b.sm_scale, True, S,
+                                    torch.from_numpy(pind).cuda(), int(pind[-1]))
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    reqs = [0, 17, 63]
+    ro, rl = omt.multi_token_attention(b, True, requests=reqs)
+    assert_close(out[reqs], ro[reqs], TOL["bf16"], "4-token out")
+    assert_lse(lse[reqs], rl[reqs], "4-token lse")
