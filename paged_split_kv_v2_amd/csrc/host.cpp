@@ -174,10 +174,11 @@ int merge_rows(const float* v_in, const float* lse_in, int num_in, const int* o_
 }
 
 // Kernel choice for one partial launch: the matrix-core paths for bf16
-// queries when a KV head serves more than 4 query rows (head dim 128 with
-// bf16 K/V) or at least 64 (MLA latent rows), and for more than 16 rows on
-// small pages; otherwise the vector path, which keeps up to 16 query rows per
-// KV head in registers and tiles more rows over several workgroups.
+// queries when a KV head serves at least 16 query rows (head dim 128 with
+// bf16 K/V; more than 16 on small pages) or at least 64 (MLA latent rows),
+// where the products are dense 16-row tiles; otherwise the vector path,
+// which keeps up to 16 query rows per KV head in registers and tiles more
+// rows over several workgroups.
 int launch_partial(const PartialArgs& a, hipStream_t stream) {
   bool handled = false;
   int st = launch_partial_latent(a, stream, &handled);

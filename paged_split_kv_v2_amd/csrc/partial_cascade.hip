@@ -44,7 +44,7 @@ void cascade_partial_kernel(const PartialArgs a0, const PartialArgs a1, const in
 
 // The fused launch covers bf16 K/V pools of head dim 128 with bf16 queries,
 // pages of a power of two >= 16 tokens, level 0 on the matrix-core body
-// (more than 4 stacked rows per KV head, as for its own launch) and level 1
+// (at least 16 stacked rows per KV head, as for its own launch) and level 1
 // on the vector body with a row tile of 4 query rows (3 or 4 rows per KV
 // head). Any other shape is left to the separate launches (*handled false).
 // (A row tile of 8 would need more registers than three workgroups per
@@ -56,7 +56,7 @@ int launch_cascade_partials(const PartialArgs& a0, const PartialArgs& a1, hipStr
     return a.q_dtype == PDK_BF16 && a.kv_dtype == PDK_BF16 && a.v != nullptr && a.Dk == 128 &&
            a.Dv == 128 && a.p_shift >= 4;
   };
-  if (!bf16_d128(a0) || !bf16_d128(a1) || a0.max_rows <= 4 || a1.member_indptr != nullptr ||
+  if (!bf16_d128(a0) || !bf16_d128(a1) || a0.max_rows < 16 || a1.member_indptr != nullptr ||
       a0.q_tokens != 1 || a1.q_tokens != 1)
     return PDK_OK;
   if (a0.S / a0.P + 1 > kMaxPagesD || a1.S / a1.P + 1 > kMaxPartPages) return PDK_OK;

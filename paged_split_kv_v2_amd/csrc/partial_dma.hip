@@ -26,19 +26,15 @@ typedef void (*DmaFn)(const PartialArgs);
 }  // namespace
 
 // bf16 K/V pools of head dim 128 (separate K and V), bf16 queries, pages of
-// a power of two >= 4 tokens, more than 4 query rows per KV head (stacked
-// level-0 rows, multi-token steps, query groups of 8 or 16): this path takes
-// the launch (*handled) with 4 waves (64 rows per row tile). With up to 4
-// rows per KV head the vector kernel streams faster (64 KB of rows in flight
-// per workgroup in registers); from 8 rows on it spends more on its
-// register-held products than the LDS ring loses (measured on a 64-request
-// step of 8 and 16 rows per KV head, before the ring took two stages at four
-// workgroups per compute unit: 277 and 283 us here against 357 and 1046 us on
-// the vector kernel).
+// a power of two >= 4 tokens, at least 16 query rows per KV head (stacked
+// level-0 rows, multi-token steps, query groups of 16): this path takes the
+// launch (*handled) with 4 waves (64 rows per row tile). Below 16 rows a
+// 16-row product tile would be partly padding - not a dense contraction -
+// and the vector kernel takes the launch.
 int launch_partial_dma(const PartialArgs& a, hipStream_t stream, bool* handled) {
   *handled = false;
   if (a.q_dtype != PDK_BF16 || a.kv_dtype != PDK_BF16 || a.v == nullptr || a.Dk != 128 ||
-      a.Dv != 128 || a.p_shift < 2 || a.max_rows <= 4)
+      a.Dv != 128 || a.p_shift < 2 || a.max_rows < 16)
     return PDK_OK;
   const int nw = 4;
   DmaFn fn = partial_dma_kernel<128, 32, 2, 4, true>;
