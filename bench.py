@@ -12,7 +12,8 @@ reused across a model's layers. Prints one JSON line.
 ``value`` is the achieved rate over the batch's unique KV bytes (each
 distinct page row read once) per step; ``roofline`` reports the dominant
 kernel with its duration measured by HIP events on the stream it is launched
-on; ``cpu_baseline`` times the f64 oracle on a bounded sample of the same
+on (one event pair around back-to-back launches of that kernel);
+``cpu_baseline`` times the f64 oracle on a bounded sample of the same
 workload on the host cores.
 """
 from __future__ import annotations
@@ -73,11 +74,11 @@ class Timer:
 
 def time_steps(torch, parts, steps, warmup):
     """Exactly `steps` steps, synchronized on both sides, each step running
-    the callables in `parts` in order with nothing else enqueued between them
-    (a timing event between two launches costs several microseconds on this
-    part). Then the same number of steps again with an event before and
-    after every part, for the mean device time of each part. Returns the wall
-    time per step of the first run (ms) and those device times (us)."""
+    the callables in `parts` in order with nothing else enqueued between them.
+    Then, for each part, its mean device time from `steps` back-to-back calls
+    of that part alone (time_launches: an event between two launches would
+    add microseconds to each). Returns the wall time per step of the first
+    run (ms) and those device times (us)."""
     for _ in range(warmup):
         for f in parts:
             f()
@@ -88,17 +89,7 @@ def time_steps(torch, parts, steps, warmup):
             f()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1000.0 / steps
-    timer = Timer(torch)
-    spans = [[] for _ in parts]
-    for _ in range(steps):
-        a = timer.mark()
-        for i, f in enumerate(parts):
-            f()
-            b = timer.mark()
-            spans[i].append((a, b))
-            a = b
-    torch.cuda.synchronize()
-    return wall_ms, [timer.mean_us(sp) for sp in spans]
+    return wall_ms, [time_launches(torch, f, steps) for f in parts]
 
 
 def time_launches(torch, f, reps):
@@ -185,14 +176,13 @@ def plan_cache_hit_us(pdk, b, params, reps=200):
 
 def run_plan_steps(args, torch, pdk, b, pool, q, plan, dev):
     """Timed steps of a planned decode: (wall ms per step, partials us, merge
-    us, cold-cache us per step, partials us from back-to-back launches)."""
+    us, cold-cache us per step)."""
     out = torch.empty((b.batch, b.num_q_heads, b.head_dim_v), dtype=torch.float32, device=dev)
     lse = torch.empty((b.batch, b.num_q_heads), dtype=torch.float32, device=dev)
     parts = [lambda: plan.run_partials(pool, q, b.sm_scale), lambda: plan.run_merge(out, lse)]
     wall_ms, (t_part, t_merge) = time_steps(torch, parts, args.steps, args.warmup)
     cold_us = time_cold(torch, parts, args.steps, dev)
-    run_us = time_launches(torch, parts[0], args.steps)
-    return wall_ms, t_part, t_merge, cold_us, run_us
+    return wall_ms, t_part, t_merge, cold_us
 
 
 def bench_flat(args, torch, pdk, W, dev):
@@ -200,8 +190,7 @@ def bench_flat(args, torch, pdk, W, dev):
     pool, csr, q = device_batch(torch, pdk, b, dev)
     S = b.partition_tokens
     plan, plan_us = planned(torch, pdk, b, pdk.CascadeParams(enabled=0, l1_partition_tokens=S), dev)
-    wall_ms, t_part, t_merge, cold_us, run_us = run_plan_steps(args, torch, pdk, b, pool, q,
-                                                               plan, dev)
+    wall_ms, t_part, t_merge, cold_us = run_plan_steps(args, torch, pdk, b, pool, q, plan, dev)
     stats, _ = plan.stats()
     R = stats["suffix_chunks"]
     Hq, Dv = b.num_q_heads, b.head_dim_v
@@ -211,7 +200,7 @@ def bench_flat(args, torch, pdk, W, dev):
     alg = (kv + b.q.nbytes + R * Hq * (Dv + 1) * 4 + b.indices.nbytes + b.kv_len.nbytes
            + (b.batch + 1) * 4)
     value = kv / (wall_ms * 1e-3) / 1e9
-    achieved = alg / (run_us * 1e-6) / 1e9
+    achieved = alg / (t_part * 1e-6) / 1e9
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 5),
@@ -231,9 +220,8 @@ def bench_flat(args, torch, pdk, W, dev):
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_record("partial_valu.hip"),
                      "kernel": "partial_valu_kernel<bf16,bf16,D128,4 rows>",
-                     "kernel_us": round(run_us, 2), "bytes_per_launch": alg},
-        "kernels_us": {"partials": round(t_part, 2), "merge": round(t_merge, 2),
-                       "partials_back_to_back": round(run_us, 2)},
+                     "kernel_us": round(t_part, 2), "bytes_per_launch": alg},
+        "kernels_us": {"partials": round(t_part, 2), "merge": round(t_merge, 2)},
         "cold_cache": {"us_per_step": round(cold_us, 2),
                        "unique_kv_GBps": round(kv / (cold_us * 1e-6) / 1e9, 2)},
     }
@@ -265,12 +253,11 @@ def bench_flat_mt(args, torch, pdk, W, dev, T=4):
              lambda: pdk.merge_states(v.view(R, T * Hq, Dv), l.view(R, T * Hq), pind_d, out, lse)]
     wall_ms, (t_part, t_merge) = time_steps(torch, parts, args.steps, args.warmup)
     cold_us = time_cold(torch, parts, args.steps, dev)
-    run_us = time_launches(torch, parts[0], args.steps)
     kv = b.unique_kv_bytes()
     alg = (kv + b.q.nbytes + R * T * Hq * (Dv + 1) * 4 + b.indices.nbytes + b.kv_len.nbytes
            + (B + 1) * 4)
     value = kv / (wall_ms * 1e-3) / 1e9
-    achieved = alg / (run_us * 1e-6) / 1e9
+    achieved = alg / (t_part * 1e-6) / 1e9
     return {"metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 5),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
@@ -291,9 +278,8 @@ def bench_flat_mt(args, torch, pdk, W, dev, T=4):
                                                    f"llama3_8b_flat_{T}_token_causal_step"),
                          "kernel": f"partial_dma_kernel<128,32,4,4> ({T * b.group} rows per "
                                    "KV head)",
-                         "kernel_us": round(run_us, 2), "bytes_per_launch": alg},
-            "kernels_us": {"partials": round(t_part, 2), "merge": round(t_merge, 2),
-                           "partials_back_to_back": round(run_us, 2)}}
+                         "kernel_us": round(t_part, 2), "bytes_per_launch": alg},
+            "kernels_us": {"partials": round(t_part, 2), "merge": round(t_merge, 2)}}
 
 
 def bench_mla_mt(args, torch, pdk, W, dev, T=4, partition_tokens=4096,
@@ -329,10 +315,10 @@ def bench_mla_mt(args, torch, pdk, W, dev, T=4, partition_tokens=4096,
     R = int(pind[-1])
     vp = torch.empty((R, T, Hq, Dv), dtype=torch.float32, device=dev)
     lp = torch.empty((R, T, Hq), dtype=torch.float32, device=dev)
-    f = lambda: pdk.paged_multi_token_partial(p_pool, p_csr, q, pre.sm_scale, False, S, pind_d,
-                                              R, vp, lp)
-    time_steps(torch, [f], args.steps, args.warmup)
-    part_us = time_launches(torch, f, args.steps)
+    _, (part_us,) = time_steps(
+        torch, [lambda: pdk.paged_multi_token_partial(p_pool, p_csr, q, pre.sm_scale, False, S,
+                                                      pind_d, R, vp, lp)],
+        args.steps, args.warmup)
     tok_pre, tok_suf = int(pre.kv_len.sum()), int(suf.kv_len.sum())
     flop_tok = 2 * Hq * (pre.head_dim_k + Dv)
     # causal suffix: token t of a request sees suffix_len - T + t + 1 positions
@@ -422,9 +408,8 @@ def bench_merge(args, torch, pdk, W, dev):
     M = len(m.o_indptr) - 1
     vo = torch.empty((M, v.shape[1], v.shape[2]), dtype=torch.float32, device=dev)
     lo = torch.empty((M, v.shape[1]), dtype=torch.float32, device=dev)
-    f = lambda: pdk.merge_states(v, l, ind, vo, lo)
-    wall_ms, _ = time_steps(torch, [f], args.steps, args.warmup)
-    dev_us = time_launches(torch, f, args.steps)
+    wall_ms, (dev_us,) = time_steps(torch, [lambda: pdk.merge_states(v, l, ind, vo, lo)],
+                                    args.steps, args.warmup)
     alg = m.v_in.nbytes + m.lse_in.nbytes + m.o_indptr.nbytes + vo.numel() * 4 + lo.numel() * 4
     value = alg / (wall_ms * 1e-3) / 1e9
     achieved = alg / (dev_us * 1e-6) / 1e9
@@ -469,9 +454,9 @@ def bench_mla(args, torch, pdk, W, dev):
     R = int(pind[-1])
     vp = torch.empty((R, Hq, Dv), dtype=torch.float32, device=dev)
     lp = torch.empty((R, Hq), dtype=torch.float32, device=dev)
-    f = lambda: pdk.paged_decode_partial(p_pool, p_csr, q, pre.sm_scale, S, pind_d, R, vp, lp)
-    time_steps(torch, [f], args.steps, args.warmup)
-    part_us = time_launches(torch, f, args.steps)
+    _, (part_us,) = time_steps(
+        torch, [lambda: pdk.paged_decode_partial(p_pool, p_csr, q, pre.sm_scale, S, pind_d, R, vp,
+                                                 lp)], args.steps, args.warmup)
     tok_pre = int(pre.kv_len.sum())
     tok_suf = int(suf.kv_len.sum())
     flop_tok = 2 * Hq * (pre.head_dim_k + Dv)
@@ -505,7 +490,7 @@ def bench_cascade(args, torch, pdk, W, dev):
     all-groups arm's partial launch (both levels in one grid)."""
     cv = bench_cascade_arms(args, torch, pdk, W, dev)
     best = cv["arms"]["cascade_all_groups"]
-    alg, part_us = cv["partial_launch_bytes"], best["partials_back_to_back_us"]
+    alg, part_us = cv["partial_launch_bytes"], best["partials_us"]
     achieved = alg / (part_us * 1e-6) / 1e9
     return {"metric": METRIC, "value": best["unique_kv_GBps"], "unit": "GB/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup,
@@ -599,14 +584,13 @@ def run_arms(args, torch, pdk, b, pool, q, dev, arms_spec, tune_base=None, bytes
                       "tuned_cold_us": round(info["us"], 2), "measured": info["measured"],
                       "tuning_s": round(time.perf_counter() - t0, 3)}
         plan, plan_us = planned(torch, pdk, b, params, dev)
-        wall_ms, t_part, t_merge, cold_us, run_us = run_plan_steps(args, torch, pdk, b, pool,
-                                                                   q, plan, dev)
+        wall_ms, t_part, t_merge, cold_us = run_plan_steps(args, torch, pdk, b, pool, q, plan,
+                                                           dev)
         stats, decline = plan.stats()
         if name == bytes_arm:
             part = cascade_partial_bytes(b, plan)
         arms[name] = {"us_per_step": round(wall_ms * 1000, 2),
                       "partials_us": round(t_part, 2), "merge_us": round(t_merge, 2),
-                      "partials_back_to_back_us": round(run_us, 2),
                       "cold_cache_us_per_step": round(cold_us, 2),
                       "unique_kv_GBps": round(kv / (wall_ms * 1e-3) / 1e9, 2),
                       "frac_of_peak": round(kv / (wall_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -680,7 +664,7 @@ def bench_nested(args, torch, pdk, W, dev):
         ("nested_spans_autotuned", None)), tune_base=base, bytes_arm="nested_spans")
     best = arms["nested_spans"]
     kv = b.unique_kv_bytes()
-    achieved = part_bytes / (best["partials_back_to_back_us"] * 1e-6) / 1e9
+    achieved = part_bytes / (best["partials_us"] * 1e-6) / 1e9
     return {"metric": METRIC, "value": best["unique_kv_GBps"], "unit": "GB/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": round(best["us_per_step"] / 1000, 5), "higher_is_better": True,
@@ -699,7 +683,7 @@ def bench_nested(args, torch, pdk, W, dev):
                          "traffic": traffic_record("partial_cascade.hip",
                                                    "nested_shared_prefix_b72"),
                          "kernel": "cascade_partial_kernel (spans + level 1 in one grid)",
-                         "kernel_us": best["partials_back_to_back_us"],
+                         "kernel_us": best["partials_us"],
                          "bytes_per_launch": part_bytes},
             "partial_state_bytes": state_bytes, "unique_kv_bytes": kv,
             "flat_read_bytes": b.read_kv_bytes(), "arms": arms,
@@ -712,8 +696,10 @@ def bench_nested(args, torch, pdk, W, dev):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # a few tens of milliseconds of warmup: the GPU's clocks settle over the
+    # first ~40 ms of back-to-back steps (shorter warmups read 5-15% slower)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="flat",
                     choices=["flat", "cascade", "merge", "mla", "copy", "flat_mt", "mla_mt",
                              "nested"])
