@@ -111,3 +111,26 @@ def test_merge_full_workload_sampled(gpu):
     src = m.o_indptr[ones]
     assert np.array_equal(vo[ones].view(np.uint32), m.v_in[src].view(np.uint32))
     assert np.array_equal(lo[ones].view(np.uint32), m.lse_in[src].view(np.uint32))
+
+
+def test_merge_groups_longer_than_one_round_trip(gpu):
+    """Groups of more than 16 rows are folded batch by batch: an all-empty
+    first batch (skipped), a maximum that first appears in a later batch
+    (running rescale), lengths on and past the batch boundaries."""
+    rng = np.random.default_rng(9)
+    counts = np.array([17, 32, 33, 40, 16, 1, 0, 48, 21, 64], dtype=np.int64)
+    ind = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    H, D = 4, 64
+    v = rng.standard_normal((ind[-1], H, D)).astype(np.float32)
+    l = rng.uniform(-4, 20, (ind[-1], H)).astype(np.float32)
+    a = ind[8]                       # group of 21: rows 0..15 empty
+    l[a:a + 16] = -np.inf
+    v[a:a + 16] = np.nan             # never read into the sum
+    b = ind[9]                       # group of 64: the largest LSEs in the last batch
+    l[b:b + 48] = rng.uniform(-30, -20, (48, H)).astype(np.float32)
+    l[b + 48:b + 64] = rng.uniform(25, 30, (16, H)).astype(np.float32)
+    vo, lo = run_merge(gpu, v, l, ind)
+    ro, rl = oatt.merge_states(np.where(np.isnan(v), 0, v), l, ind)
+    assert np.all(np.isfinite(vo))
+    assert_close(vo, ro, 1e-5, "merge out")
+    assert_lse(lo, rl, "merge lse")
