@@ -155,3 +155,18 @@ def test_full_size_four_token_step_sampled(gpu):
     ro, rl = omt.multi_token_attention(b, True, requests=reqs)
     assert_close(out[reqs], ro[reqs], TOL["bf16"], "4-token out")
     assert_lse(lse[reqs], rl[reqs], "4-token lse")
+
+
+def test_full_size_four_token_mla_step_sampled(gpu):
+    """The benchmark's 4-token MLA step at its full size (batch 32, 128
+    heads, 16384 cached fp8 tokens in 4096-token chunks and partitions, 256
+    bf16 suffix tokens in one partition, one merge): sampled requests
+    against the definition, every output finite."""
+    share = W.mla_share_with_query_tokens(
+        W.mla_decode_share(partition_tokens=4096, suffix_partition_tokens=256), 4, 1007)
+    out, lse = run_mla_mt(gpu, share, staged=False)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    reqs = [0, 21]
+    ro, rl = omt.mla_multi_token_flat(share, requests=reqs)
+    assert_close(out[reqs], ro[reqs], TOL["fp8_e4m3"], "4-token mla out")
+    assert_lse(lse[reqs], rl[reqs], "4-token mla lse")
