@@ -100,6 +100,185 @@ struct Tile {
   int tok[T];  // position of each token (read only with causal rows)
 };
 
+// Registers of a row's query: bf16 pairs for the dot2 path, else one f32
+// per element.
+template <int KT, int QT, int D>
+struct QueryWords {
+  static constexpr int value = (KT == KV_BF16 && QT == PDK_BF16) ? D / 32 : D / 16;
+};
+
+// One step of T tokens per row group for the GM owned query rows: q.k dots
+// summed over the 16-lane row group (DPP, one stage at a time across all
+// values), scores of invalid (or, causal, invisible) tokens masked to -inf,
+// the online softmax in log2 units with a lazily raised reference maximum
+// (raised only when a score exceeds it by more than kLazyLog2), and
+// acc += p * v with each stored pair of V widened just before its use.
+template <int KT, int QT, int D, int GM, bool CAUSAL, int NU, int T>
+__device__ __forceinline__ void valu_step(const Tile<NU, T>& X,
+                                          const uint32_t (&qw)[GM][QueryWords<KT, QT, D>::value],
+                                          const int (&lim)[GM], float scale_log2,
+                                          float (&run_m)[GM], float (&run_l)[GM],
+                                          float (&acc)[GM][D / 16]) {
+  constexpr int E = D / 16;
+  constexpr bool kDot2 = (KT == KV_BF16 && QT == PDK_BF16);
+  constexpr int QW = QueryWords<KT, QT, D>::value;
+  float s[T * GM];
+#pragma unroll
+  for (int u = 0; u < T; ++u) {
+    float kf[E];
+    if constexpr (!kDot2) widen<KT, E, NU>(X.kw[u], kf);
+#pragma unroll
+    for (int gi = 0; gi < GM; ++gi) {
+      float d = 0.f;
+      if constexpr (kDot2) {
+#pragma unroll
+        for (int i = 0; i < QW; ++i)
+          d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qw[gi][i]),
+                                              __builtin_bit_cast(bf16x2_t, X.kw[u][i]), d, false);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) d = fmaf(bits_f32(qw[gi][e]), kf[e], d);
+      }
+      s[u * GM + gi] = d;
+    }
+  }
+  row16_sum_n<T * GM>(s);
+#pragma unroll
+  for (int u = 0; u < T; ++u)
+#pragma unroll
+    for (int gi = 0; gi < GM; ++gi)
+      s[u * GM + gi] = (X.valid[u] && (!CAUSAL || X.tok[u] < lim[gi]))
+                           ? s[u * GM + gi] * scale_log2 : -INFINITY;
+
+  // raise the reference maxima only where a score jumped past them
+  float mx[GM];
+  int need = 0;
+#pragma unroll
+  for (int gi = 0; gi < GM; ++gi) {
+    mx[gi] = s[gi];
+#pragma unroll
+    for (int u = 1; u < T; ++u) mx[gi] = fmaxf(mx[gi], s[u * GM + gi]);
+    need |= mx[gi] > run_m[gi] + kLazyLog2;
+  }
+  if (__any(need)) {
+#pragma unroll
+    for (int gi = 0; gi < GM; ++gi) {
+      const float mn = (mx[gi] > run_m[gi] + kLazyLog2) ? mx[gi] : run_m[gi];
+      const float corr = (mn == run_m[gi]) ? 1.f : fast_exp2(run_m[gi] - mn);
+      run_l[gi] *= corr;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[gi][e] *= corr;
+      run_m[gi] = mn;
+    }
+  }
+#pragma unroll
+  for (int gi = 0; gi < GM; ++gi) {
+    const float mu = (run_m[gi] == -INFINITY) ? 0.f : run_m[gi];
+    float psum = 0.f;
+#pragma unroll
+    for (int u = 0; u < T; ++u) {
+      s[u * GM + gi] = fast_exp2(s[u * GM + gi] - mu);
+      psum += s[u * GM + gi];
+    }
+    run_l[gi] += psum;
+  }
+#pragma unroll
+  for (int u = 0; u < T; ++u) {
+    if constexpr (KT == KV_F32) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float v = bits_f32(X.vw[u][e]);
+#pragma unroll
+        for (int gi = 0; gi < GM; ++gi) acc[gi][e] = fmaf(s[u * GM + gi], v, acc[gi][e]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < E / 2; ++i) {
+        const float v0 = bf16_lo(X.vw[u][i]), v1 = bf16_hi(X.vw[u][i]);
+#pragma unroll
+        for (int gi = 0; gi < GM; ++gi) {
+          acc[gi][2 * i] = fmaf(s[u * GM + gi], v0, acc[gi][2 * i]);
+          acc[gi][2 * i + 1] = fmaf(s[u * GM + gi], v1, acc[gi][2 * i + 1]);
+        }
+      }
+    }
+  }
+}
+
+// Exact merge of the four row groups of a wave (lanes l, l^16, l^32, l^48):
+// every lane leaves with the wave's (max, sum, accumulator) of each row.
+template <int GM, int E>
+__device__ __forceinline__ void valu_wave_merge(float (&run_m)[GM], float (&run_l)[GM],
+                                                float (&acc)[GM][E]) {
+#pragma unroll
+  for (int gi = 0; gi < GM; ++gi) {
+    float mw = fmaxf(run_m[gi], __shfl_xor(run_m[gi], 16));
+    mw = fmaxf(mw, __shfl_xor(mw, 32));
+    const float mu = (mw == -INFINITY) ? 0.f : mw;
+    const float w = fast_exp2(run_m[gi] - mu);
+    float l = run_l[gi] * w;
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      float x = acc[gi][e] * w;
+      x += __shfl_xor(x, 16);
+      x += __shfl_xor(x, 32);
+      acc[gi][e] = x;
+    }
+    run_m[gi] = mw;
+    run_l[gi] = l;
+  }
+}
+
+// The wave's merged states into LDS (the first row group of each wave).
+template <int GM, int D>
+__device__ __forceinline__ void valu_publish(float (&sm_acc)[4][GM][D], float (&sm_m)[4][GM],
+                                             float (&sm_l)[4][GM], const float (&run_m)[GM],
+                                             const float (&run_l)[GM],
+                                             const float (&acc)[GM][D / 16]) {
+  constexpr int E = D / 16;
+  const int wave = threadIdx.x >> 6, j = threadIdx.x & 15;
+  if ((threadIdx.x & 63) < 16) {
+#pragma unroll
+    for (int gi = 0; gi < GM; ++gi) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) sm_acc[wave][gi][j * E + e] = acc[gi][e];
+      if (j == 0) {
+        sm_m[wave][gi] = run_m[gi];
+        sm_l[wave][gi] = run_l[gi];
+      }
+    }
+  }
+}
+
+// Merge of the four waves' states (after a barrier) and the normalized
+// partial and LSE of each of the first n_live rows: store(gi, d, value, lse)
+// writes element d of row gi (lse on d == 0).
+template <int GM, int D, typename Store>
+__device__ __forceinline__ void valu_finish(const float (&sm_acc)[4][GM][D],
+                                            const float (&sm_m)[4][GM],
+                                            const float (&sm_l)[4][GM], int Dv, int n_live,
+                                            Store store) {
+  for (int idx = threadIdx.x; idx < GM * Dv; idx += kThreads) {
+    const int gi = idx / Dv;
+    const int d = idx - gi * Dv;
+    if (gi >= n_live) continue;
+    float M = sm_m[0][gi];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, sm_m[w][gi]);
+    const float Mu = (M == -INFINITY) ? 0.f : M;
+    float L = 0.f, num = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float ww = fast_exp2(sm_m[w][gi] - Mu);
+      L = fmaf(ww, sm_l[w][gi], L);
+      num = fmaf(ww, sm_acc[w][gi][d], num);
+    }
+    store(gi, d, (L > 0.f) ? num / L : 0.f, (L > 0.f) ? M + log2f(L) : -INFINITY);
+  }
+}
+
 // The work of one workgroup of 256 threads: `block` is its index in the
 // grid of its launch (the decomposition below is over that index).
 template <int KT, int QT, int D, int GM, bool UNIF, bool CAUSAL>
@@ -107,7 +286,7 @@ __device__ __forceinline__ void partial_valu_body(const PartialArgs& a, const in
   constexpr int E = D / 16;                          // elements per lane
   constexpr int NU = E * (KT == KV_F32 ? 4 : 2) / 4; // 32-bit words per lane per row
   constexpr bool kDot2 = (KT == KV_BF16 && QT == PDK_BF16);
-  constexpr int QW = kDot2 ? E / 2 : E;              // per-row query registers
+  constexpr int QW = QueryWords<KT, QT, D>::value;  // per-row query registers
   constexpr int ESZ = (KT == KV_F32) ? 4 : 2;
   constexpr int T = TokPerRowGroup<GM, E>::value;
   constexpr int kStep = 16 * T;  // tokens per step of the workgroup
@@ -250,90 +429,7 @@ __device__ __forceinline__ void partial_valu_body(const PartialArgs& a, const in
   };
 
   auto compute_step = [&](const Tile<NU, T>& X) {
-    // q.k partial dots, summed over the row group one DPP stage at a time
-    float s[T * GM];
-#pragma unroll
-    for (int u = 0; u < T; ++u) {
-      float kf[E];
-      if constexpr (!kDot2) widen<KT, E, NU>(X.kw[u], kf);
-#pragma unroll
-      for (int gi = 0; gi < GM; ++gi) {
-        float d = 0.f;
-        if constexpr (kDot2) {
-#pragma unroll
-          for (int i = 0; i < QW; ++i)
-            d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qw[gi][i]),
-                                                __builtin_bit_cast(bf16x2_t, X.kw[u][i]), d,
-                                                false);
-        } else {
-#pragma unroll
-          for (int e = 0; e < E; ++e) d = fmaf(bits_f32(qw[gi][e]), kf[e], d);
-        }
-        s[u * GM + gi] = d;
-      }
-    }
-    row16_sum_n<T * GM>(s);
-#pragma unroll
-    for (int u = 0; u < T; ++u)
-#pragma unroll
-      for (int gi = 0; gi < GM; ++gi)
-        s[u * GM + gi] = (X.valid[u] && (!CAUSAL || X.tok[u] < lim[gi]))
-                             ? s[u * GM + gi] * a.scale_log2 : -INFINITY;
-
-    // raise the reference maxima only where a score jumped past them
-    float mx[GM];
-    int need = 0;
-#pragma unroll
-    for (int gi = 0; gi < GM; ++gi) {
-      mx[gi] = s[gi];
-#pragma unroll
-      for (int u = 1; u < T; ++u) mx[gi] = fmaxf(mx[gi], s[u * GM + gi]);
-      need |= mx[gi] > run_m[gi] + kLazyLog2;
-    }
-    if (__any(need)) {
-#pragma unroll
-      for (int gi = 0; gi < GM; ++gi) {
-        const float mn = (mx[gi] > run_m[gi] + kLazyLog2) ? mx[gi] : run_m[gi];
-        const float corr = (mn == run_m[gi]) ? 1.f : fast_exp2(run_m[gi] - mn);
-        run_l[gi] *= corr;
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[gi][e] *= corr;
-        run_m[gi] = mn;
-      }
-    }
-#pragma unroll
-    for (int gi = 0; gi < GM; ++gi) {
-      const float mu = (run_m[gi] == -INFINITY) ? 0.f : run_m[gi];
-      float psum = 0.f;
-#pragma unroll
-      for (int u = 0; u < T; ++u) {
-        s[u * GM + gi] = fast_exp2(s[u * GM + gi] - mu);
-        psum += s[u * GM + gi];
-      }
-      run_l[gi] += psum;
-    }
-    // acc += p * v, widening each stored pair of V just before its use
-#pragma unroll
-    for (int u = 0; u < T; ++u) {
-      if constexpr (KT == KV_F32) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const float v = bits_f32(X.vw[u][e]);
-#pragma unroll
-          for (int gi = 0; gi < GM; ++gi) acc[gi][e] = fmaf(s[u * GM + gi], v, acc[gi][e]);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < E / 2; ++i) {
-          const float v0 = bf16_lo(X.vw[u][i]), v1 = bf16_hi(X.vw[u][i]);
-#pragma unroll
-          for (int gi = 0; gi < GM; ++gi) {
-            acc[gi][2 * i] = fmaf(s[u * GM + gi], v0, acc[gi][2 * i]);
-            acc[gi][2 * i + 1] = fmaf(s[u * GM + gi], v1, acc[gi][2 * i + 1]);
-          }
-        }
-      }
-    }
+    valu_step<KT, QT, D, GM, CAUSAL>(X, qw, lim, a.scale_log2, run_m, run_l, acc);
   };
 
   // two register tiles: the next step's rows are requested before the
@@ -354,57 +450,17 @@ __device__ __forceinline__ void partial_valu_body(const PartialArgs& a, const in
     if (!more2) break;
   }
 
-  // merge the four row groups of this wave (lanes l, l^16, l^32, l^48)
-  const int wave = tid >> 6;
-#pragma unroll
-  for (int gi = 0; gi < GM; ++gi) {
-    float mw = fmaxf(run_m[gi], __shfl_xor(run_m[gi], 16));
-    mw = fmaxf(mw, __shfl_xor(mw, 32));
-    const float mu = (mw == -INFINITY) ? 0.f : mw;
-    const float w = fast_exp2(run_m[gi] - mu);
-    float l = run_l[gi] * w;
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      float x = acc[gi][e] * w;
-      x += __shfl_xor(x, 16);
-      x += __shfl_xor(x, 32);
-      acc[gi][e] = x;
-    }
-    if ((tid & 63) < 16) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) sm_acc[wave][gi][j * E + e] = acc[gi][e];
-      if (j == 0) {
-        sm_m[wave][gi] = mw;
-        sm_l[wave][gi] = l;
-      }
-    }
-  }
+  valu_wave_merge(run_m, run_l, acc);
+  valu_publish(sm_acc, sm_m, sm_l, run_m, run_l, acc);
   __syncthreads();
-
   // merge the four waves and write the normalized partial and its LSE
-  for (int idx = tid; idx < GM * a.Dv; idx += kThreads) {
-    const int gi = idx / a.Dv;
-    const int d = idx - gi * a.Dv;
+  valu_finish(sm_acc, sm_m, sm_l, a.Dv, nrows - row0, [&](int gi, int d, float v, float lse) {
     const int row = row0 + gi;
-    if (row >= nrows) continue;
-    float M = sm_m[0][gi];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, sm_m[w][gi]);
-    const float Mu = (M == -INFINITY) ? 0.f : M;
-    float L = 0.f, num = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float ww = fast_exp2(sm_m[w][gi] - Mu);
-      L = fmaf(ww, sm_l[w][gi], L);
-      num = fmaf(ww, sm_acc[w][gi][d], num);
-    }
     const int m = row / a.G, g = row % a.G;
     const size_t o = state_index(a, stacked, mbase, b, p, m, h * a.G + g);
-    a.v_out[o * a.Dv + d] = (L > 0.f) ? num / L : 0.f;
-    if (d == 0) a.lse_out[o] = (L > 0.f) ? M + log2f(L) : -INFINITY;
-  }
+    a.v_out[o * a.Dv + d] = v;
+    if (d == 0) a.lse_out[o] = lse;
+  });
 }
 
 }  // namespace
