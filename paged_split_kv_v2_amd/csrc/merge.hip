@@ -14,9 +14,10 @@
 // maximum, so a group of up to 16 rows costs one memory round trip. The
 // waves of a workgroup take independent (output row, 256-float span) units.
 // (Measured on 8192 output rows of 32 x 128 floats, 1-16 rows per group:
-// sixteen rows per round trip 228 us against 243 us for eight; issuing the
-// loads from scalar row bases cuts registers to four waves per SIMD but runs
-// slower, 235 us, and so does a grid-stride loop over units, 269 us.)
+// sixteen rows per round trip 228 us against 243 us for eight, 219 us with
+// non-temporal loads and stores; issuing the loads from scalar row bases cuts
+// registers to four waves per SIMD but runs slower, 235 us, and so does a
+// grid-stride loop over units, 269 us.)
 
 #include "device.h"
 #include "internal.h"
@@ -24,6 +25,15 @@
 namespace pdk {
 
 namespace {
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Input rows are read once and output rows written once: non-temporal
+// (streaming) loads and stores.
+__device__ __forceinline__ float4 load_nt(const float* p) {
+  const f32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+  return make_float4(t[0], t[1], t[2], t[3]);
+}
 
 constexpr int kMergeThreads = 256;  // four independent waves per workgroup
 constexpr int kMergeSpan = 64 * 4;  // floats of an output row per wave
@@ -52,7 +62,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
   const float lse0 = n > 0 ? lrow[0] : -INFINITY;
   if (n == 1 && lse0 != -INFINITY) {
     // identity, bit for bit
-    out = *reinterpret_cast<const float4*>(v_in + (size_t)a * HD + e);
+    out = load_nt(v_in + (size_t)a * HD + e);
     lse = lse0;
   } else if (n > 1) {
     // one pass in batches of kMergeBatch rows: the batch's LSEs and value
@@ -60,8 +70,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
     // groups of at most kMergeBatch rows this is the plain two-step merge)
     float m = -INFINITY, l = 0.f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    const float4* vrow = reinterpret_cast<const float4*>(v_in + (size_t)a * HD + e);
-    const size_t vstep = (size_t)HD / 4;
+    const float* vrow = v_in + (size_t)a * HD + e;
     for (int r0 = 0; r0 < n; r0 += kMergeBatch) {
       float w[kMergeBatch];
       float4 x[kMergeBatch];
@@ -69,7 +78,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
       for (int k = 0; k < kMergeBatch; ++k) {
         const bool in = r0 + k < n;
         w[k] = in ? lrow[(size_t)(r0 + k) * H] : -INFINITY;
-        x[k] = in ? vrow[(size_t)(r0 + k) * vstep] : make_float4(0.f, 0.f, 0.f, 0.f);
+        x[k] = in ? load_nt(vrow + (size_t)(r0 + k) * HD) : make_float4(0.f, 0.f, 0.f, 0.f);
       }
       float bm = w[0];
 #pragma unroll
@@ -97,7 +106,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
       lse = m + log2f(l);
     }
   }
-  *reinterpret_cast<float4*>(v_out + orow) = out;
+  __builtin_nontemporal_store(f32x4_t{out.x, out.y, out.z, out.w},
+                              reinterpret_cast<f32x4_t*>(v_out + orow));
   if (lse_out != nullptr && (e - head * D) == 0) lse_out[(size_t)i * out_stride * H + head] = lse;
 }
 
