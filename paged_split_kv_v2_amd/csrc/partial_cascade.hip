@@ -23,6 +23,12 @@ namespace {
 
 constexpr int kL0Waves = 4;  // level-0 body: 4 waves x 16 stacked query rows
 constexpr int kL0Stages = 2;  // level-0 LDS ring: two 32-token stages
+// Level-0 rows with ordinary (cached) loads: a step's unique bytes (0.28 GB
+// on the 72-request shared-prefix step) largely fit the last-level cache, and
+// non-temporal fetches there cost 51.4 -> 54.1 us when steps run back to
+// back. (The level-1 body keeps its non-temporal loads: cached ones gained
+// nothing back to back and cost 67.5 -> 72.3 us with a cold cache.)
+constexpr bool kL0Streaming = false;
 static_assert(64 * kL0Waves == kThreads, "both bodies run on 256-thread workgroups");
 
 // Three workgroups per compute unit: the level-1 body alone fits three (156
@@ -35,7 +41,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void cascade_partial_kernel(const PartialArgs a0, const PartialArgs a1, const int blocks0) {
   const int bid = blockIdx.x;
   if (bid < blocks0)
-    partial_dma_body<128, 32, kL0Stages, kL0Waves, true>(a0, bid);
+    partial_dma_body<128, 32, kL0Stages, kL0Waves, true, kL0Streaming>(a0, bid);
   else
     partial_valu_body<KV_BF16, PDK_BF16, 128, 4, true, false>(a1, bid - blocks0);
 }

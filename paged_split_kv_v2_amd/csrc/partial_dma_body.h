@@ -58,6 +58,9 @@ __device__ __forceinline__ int dswz(int t) {
   return ((t & 3) << 1) | ((t >> 2) & 1) | (t & 8);
 }
 
+// Cache-policy operand of a global->LDS load that marks it non-temporal.
+constexpr int kCachePolicyNT = 2;
+
 // s_waitcnt vmcnt(N), other counters untouched.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -67,8 +70,9 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 // The work of one workgroup of 64 * NW threads: `block` is its index in the
-// grid of its launch (the decomposition below is over that index).
-template <int D, int TT, int NS, int NW, bool SPLIT>
+// grid of its launch (the decomposition below is over that index). NT: the
+// K/V fetches are non-temporal (streaming) loads.
+template <int D, int TT, int NS, int NW, bool SPLIT, bool NT>
 __device__ __forceinline__ void partial_dma_body(const PartialArgs& a, const int block) {
   constexpr int KS = D / 32;                 // k-steps of S^T
   constexpr int TB = TT / 16;                // 16-token blocks per tile
@@ -189,7 +193,7 @@ __device__ __forceinline__ void partial_dma_body(const PartialArgs& a, const int
       const char* src = (is_v ? vbase + pid * vbs : kbase + pid * kbs) + (tc & pmask) * (2 * D) + q * 16;
       __builtin_amdgcn_global_load_lds(
           src, (__attribute__((address_space(3))) void*)(dst + (is_v ? TT * D : 0) + 512 * mm),
-          16, 0, 0);
+          16, 0, NT ? kCachePolicyNT : 0);
     }
   };
 
