@@ -1,0 +1,130 @@
+"""Argument checks of the C ABI (no GPU work): every call below must be
+refused on the host, before any launch or copy, with the documented status
+and a message. Device pointers are stand-in addresses that are never
+dereferenced when the checks hold. The module is skipped where a GPU is
+visible, so that a missing check could never send those addresses to a
+kernel."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import paged_split_kv_v2_amd as pdk
+
+if torch.cuda.device_count() > 0:
+    pytest.skip("host-side argument checks run where no GPU is visible", allow_module_level=True)
+
+ERR_ARG, ERR_SHAPE, ERR_WORKSPACE = -1, -2, -5
+FAKE = 0x100000  # 16-byte aligned stand-in for a device address
+
+
+def lib():
+    return pdk.lib()
+
+
+BF16 = 1  # pdk_dtype
+
+
+def pool(P=16, Hkv=2, D=64, dtype=BF16):
+    return pdk._Pool(k=FAKE, v=FAKE, num_blocks=64, page_size=P, num_kv_heads=Hkv,
+                     head_dim_k=D, head_dim_v=D, dtype=dtype, k_scale=1.0, v_scale=1.0)
+
+
+def dev_csr(batch=2):
+    return pdk._CSR(indptr=FAKE, indices=FAKE, kv_len=FAKE, batch=batch, nnz=8)
+
+
+def status(rc, code, word):
+    assert rc == code, (rc, lib().pdk_last_error())
+    assert word.encode() in lib().pdk_last_error().lower(), lib().pdk_last_error()
+
+
+def test_multi_token_partial_rejects_bad_token_count_and_causal_flag():
+    p, c = pool(), dev_csr()
+    for T, causal in ((0, 1), (2, 2)):
+        rc = lib().pdk_paged_multi_token_partial(ctypes.byref(p), ctypes.byref(c), FAKE, 1, 4, T,
+                                                 causal, 0.125, 32, FAKE, 4, FAKE, FAKE, None)
+        status(rc, ERR_ARG, "q_tokens")
+
+
+def test_partition_size_must_be_a_multiple_of_the_page():
+    p, c = pool(), dev_csr()
+    rc = lib().pdk_paged_decode_partial(ctypes.byref(p), ctypes.byref(c), FAKE, 1, 4, 0.125, 24,
+                                        FAKE, 4, FAKE, FAKE, None)
+    status(rc, ERR_ARG, "multiple of page_size")
+
+
+def test_flat_decode_rejects_a_small_workspace():
+    p, c = pool(), dev_csr()
+    need = lib().pdk_decode_flat_workspace_bytes(4, 4, 64)
+    assert need > 0
+    rc = lib().pdk_decode_flat(ctypes.byref(p), ctypes.byref(c), FAKE, 1, 4, 0.125, 32, FAKE, 4,
+                               FAKE, FAKE, FAKE, need - 1, None)
+    status(rc, ERR_WORKSPACE, "workspace")
+    rc = lib().pdk_multi_token_flat(ctypes.byref(p), ctypes.byref(c), FAKE, 1, 4, 2, 1, 0.125, 32,
+                                    FAKE, 4, FAKE, FAKE, FAKE,
+                                    lib().pdk_decode_flat_workspace_bytes(4, 8, 64) - 1, None)
+    status(rc, ERR_WORKSPACE, "workspace")
+
+
+def host_csr(lists, lens):
+    indptr = np.cumsum([0] + [len(x) for x in lists]).astype(np.int32)
+    indices = np.asarray([p for x in lists for p in x], np.int32)
+    kv_len = np.asarray(lens, np.int32)
+    keep = (indptr, indices, kv_len)
+    return pdk._CSR(indptr=indptr.ctypes.data, indices=indices.ctypes.data,
+                    kv_len=kv_len.ctypes.data, batch=len(lens), nnz=int(indptr[-1])), keep
+
+
+def params(**kw):
+    pr = pdk._Params()
+    lib().pdk_cascade_params_default(ctypes.byref(pr))
+    for k, v in kw.items():
+        setattr(pr, k, v)
+    return pr
+
+
+@pytest.mark.parametrize("kw,word", [
+    (dict(l1_partition_tokens=24), "multiples of page_size"),
+    (dict(l0_partition_tokens=0), "multiples of page_size"),
+    (dict(min_members=1), "thresholds"),
+    (dict(fuse_levels=2), "fuse_levels"),
+])
+def test_cascade_plan_rejects_bad_parameters(kw, word):
+    c, keep = host_csr([[0, 1, 2], [0, 1, 3]], [40, 40])
+    plan = ctypes.c_void_p()
+    rc = lib().pdk_cascade_plan_create(ctypes.byref(c), 16, ctypes.byref(params(**kw)),
+                                       ctypes.byref(plan))
+    status(rc, ERR_ARG, word)
+    assert not plan.value
+
+
+def test_cascade_plan_must_be_uploaded_to_the_workspace_it_runs_from():
+    c, keep = host_csr([[0, 1, 2], [0, 1, 3]], [40, 40])
+    plan = ctypes.c_void_p()
+    assert lib().pdk_cascade_plan_create(ctypes.byref(c), 16,
+                                         ctypes.byref(params(enabled=1, min_shared_pages=1)),
+                                         ctypes.byref(plan)) == 0
+    try:
+        p = pool()
+        need = lib().pdk_cascade_workspace_bytes(plan, 4, 64)
+        assert need > 0
+        # too small to upload into: refused before the copy
+        status(lib().pdk_cascade_plan_upload(plan, FAKE, 16, None), ERR_WORKSPACE, "workspace")
+        # never uploaded: the run is refused
+        rc = lib().pdk_run_cascade_decode(plan, ctypes.byref(p), FAKE, 1, 4, 0.125, FAKE, FAKE,
+                                          FAKE, need, None)
+        status(rc, ERR_WORKSPACE, "uploaded")
+    finally:
+        lib().pdk_cascade_plan_free(plan)
+
+
+def test_page_table_checks_name_the_violation():
+    # page count disagrees with the length; an id outside the pool
+    for lists, lens in (([[0, 1], [2]], [40, 10]), ([[0, 1, 9], [2]], [40, 10])):
+        c, keep = host_csr(lists, lens)
+        assert lib().pdk_validate_csr(ctypes.byref(c), 16, 8) == ERR_SHAPE
+        assert lib().pdk_last_error()
+    c, keep = host_csr([[0, 1, 2], [3]], [40, 10])
+    assert lib().pdk_validate_csr(ctypes.byref(c), 16, 8) == 0
