@@ -14,7 +14,7 @@ distinct page row read once) per step; ``roofline`` reports the dominant
 kernel with its duration measured by HIP events on the stream it is launched
 on (one event pair around back-to-back launches of that kernel);
 ``cpu_baseline`` times the f64 oracle on a bounded sample of the same
-workload on the host cores.
+workload on one host thread (10-15 s, in the line's unit).
 """
 from __future__ import annotations
 
@@ -131,31 +131,82 @@ def time_cold(torch, parts, steps, dev):
     return timer.mean_us(spans)
 
 
-def cpu_baseline(batches, min_s=10.0, budget_s=15.0):
-    """The f64 oracle, whole requests with all heads, on a bounded sample:
-    GB of KV attended per second on one host thread. Requests are taken in
-    a seeded order, in repeated passes over the batch until at least min_s
-    seconds have run, and never past budget_s."""
+def oracle_rate(units, run, amount, unit, scale, what, min_s=10.0, budget_s=15.0):
+    """The f64 oracle as it stands, timed on one host thread over a bounded
+    sample of the workload: the units (in a seeded order) are run one at a
+    time, in repeated passes until at least min_s seconds have run and never
+    past budget_s; value = the units' summed amount per second / scale."""
     import threadpoolctl
-    from oracle import attention as oatt
-    done, kv_bytes = 0, 0
+    order = [units[i] for i in np.random.default_rng(0).permutation(len(units))]
+    done, total = 0, 0.0
     t0 = time.perf_counter()
     with threadpoolctl.threadpool_limits(1):
         while time.perf_counter() - t0 < min_s:
-            for b in batches:
-                for r in np.random.default_rng(0).permutation(b.batch):
-                    oatt.decode_attention(b, requests=[int(r)])
-                    done += 1
-                    kv_bytes += int(b.kv_len[r]) * b.kv_bytes_per_token()
-                    if time.perf_counter() - t0 > budget_s:
-                        break
+            for u in order:
+                run(u)
+                done += 1
+                total += amount(u)
                 if time.perf_counter() - t0 > budget_s:
                     break
+            if time.perf_counter() - t0 > budget_s:
+                break
     dt = time.perf_counter() - t0
-    n_req = sum(b.batch for b in batches)
-    return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} requests of the same workload ({done / n_req:.2f} passes over its "
-                      f"{n_req} requests, all heads), f64 numpy oracle on one thread, {dt:.1f} s"}
+    return {"value": round(total / dt / scale, 4), "unit": unit, "cores": 1, "kind": "oracle",
+            "sample": f"{done} {what} ({done / len(units):.2f} passes over the workload's "
+                      f"{len(units)}), f64 numpy oracle on one thread, {dt:.1f} s"}
+
+
+def cpu_baseline(b):
+    """The oracle's flat decode, one whole request (all heads) at a time: GB
+    of KV attended per second."""
+    from oracle import attention as oatt
+    return oracle_rate(list(range(b.batch)), lambda r: oatt.decode_attention(b, requests=[r]),
+                       lambda r: int(b.kv_len[r]) * b.kv_bytes_per_token(), "GB/s", 1e9,
+                       "requests (all heads)")
+
+
+def baseline_for(workload, x):
+    """The oracle timed on the workload the GPU line measured (x: its
+    inputs), in the line's unit."""
+    from oracle import attention as oatt
+    if workload in ("cascade", "nested"):
+        from oracle import cascade as ocas, nested as onest, planner as opl
+        p = opl.CascadeParams(enabled=1, max_groups=0, l0_partition_tokens=1024,
+                              l1_partition_tokens=512)
+        run = ((lambda _: ocas.cascade_decode(x, p)) if workload == "cascade"
+               else (lambda _: onest.nested_cascade_decode(x, p, 2)))
+        return oracle_rate([0], run, lambda _: x.unique_kv_bytes(), "GB/s", 1e9,
+                           f"whole-batch {workload} decodes")
+    if workload == "merge":
+        ind, H, D = x.o_indptr, x.v_in.shape[1], x.v_in.shape[2]
+        M = len(ind) - 1
+        def run(u):
+            a, e = int(ind[u]), int(ind[min(u + 64, M)])
+            oatt.merge_states(x.v_in[a:e], x.lse_in[a:e], ind[u:min(u + 64, M) + 1] - a)
+        def amount(u):
+            rows = int(ind[min(u + 64, M)] - ind[u]) + min(64, M - u)
+            return rows * H * (D + 1) * 4
+        return oracle_rate(list(range(0, M, 64)), run, amount, "GB/s", 1e9,
+                           "blocks of 64 output rows")
+    if workload == "flat_mt":
+        from oracle import multitoken as omt
+        return oracle_rate(list(range(x.batch)),
+                           lambda r: omt.multi_token_attention(x, True, requests=[r]),
+                           lambda r: int(x.kv_len[r]) * x.kv_bytes_per_token(), "GB/s", 1e9,
+                           "requests (all tokens and heads)")
+    if workload in ("mla", "mla_mt"):
+        from oracle import mla as omla, multitoken as omt
+        pre, suf = x.prefix, x.suffix
+        T = x.prefix.q.shape[1] if workload == "mla_mt" else 1
+        flop_tok = 2 * pre.num_q_heads * (pre.head_dim_k + pre.head_dim_v)
+        def amount(r):
+            n = int(suf.kv_len[r])
+            return flop_tok * (T * int(pre.kv_len[r]) + T * n - T * (T - 1) // 2)
+        run = ((lambda r: omla.mla_flat(x, requests=[r])) if workload == "mla"
+               else (lambda r: omt.mla_multi_token_flat(x, requests=[r])))
+        return oracle_rate(list(range(pre.batch)), run, amount, "TFLOP/s", 1e12,
+                           "requests (all heads)")
+    return None
 
 
 def planned(torch, pdk, b, params, dev):
@@ -231,11 +282,10 @@ def bench_flat(args, torch, pdk, W, dev):
         "cold_cache": {"us_per_step": round(cold_us, 2),
                        "unique_kv_GBps": round(kv / (cold_us * 1e-6) / 1e9, 2)},
     }
-    batches = [b]
     if not args.no_cascade:
         res["cascade_vs_flat"] = bench_cascade_arms(args, torch, pdk, W, dev)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(batches)
+        res["cpu_baseline"] = cpu_baseline(b)
     return res
 
 
@@ -245,6 +295,7 @@ def bench_flat_mt(args, torch, pdk, W, dev, T=4):
     partials of every (request, partition, token, head), then one merge per
     request over the (token, head) pairs."""
     b = W.with_query_tokens(W.llama3_8b_flat(), T, 1006)
+    args.inputs = b
     pool, csr, q = device_batch(torch, pdk, b, dev)
     S = b.partition_tokens
     pind = pdk.partition_indptr(b.kv_len, S)
@@ -300,6 +351,7 @@ def bench_mla_mt(args, torch, pdk, W, dev, T=4, partition_tokens=4096,
         W.mla_decode_share(partition_tokens=partition_tokens,
                            suffix_partition_tokens=suffix_partition_tokens), T, 1007)
     pre, suf = share.prefix, share.suffix
+    args.inputs = share
     p_pool, p_csr, q = device_batch(torch, pdk, pre, dev)
     s_pool, _, _ = device_batch(torch, pdk, suf, dev)
     plan = pdk.ChunkedPlan((pre.indptr, pre.indices, pre.kv_len), pre.page_size,
@@ -408,6 +460,7 @@ def traffic_record(kernel_source, workload=None):
 def bench_merge(args, torch, pdk, W, dev):
     """merge_states on 8192 output rows, H 32, D 128, 1..16 rows per group."""
     m = W.merge_microbench()
+    args.inputs = m
     v = torch.from_numpy(m.v_in).to(dev)
     l = torch.from_numpy(m.lse_in).to(dev)
     ind = torch.from_numpy(m.o_indptr).to(dev)
@@ -439,6 +492,7 @@ def bench_mla(args, torch, pdk, W, dev):
     whole pipeline: chunk partials, per-chunk merge, merge across chunks,
     suffix partials and merge, final merge."""
     share = W.mla_decode_share()
+    args.inputs = share
     pre, suf = share.prefix, share.suffix
     p_pool, p_csr, q = device_batch(torch, pdk, pre, dev)
     s_pool, _, _ = device_batch(torch, pdk, suf, dev)
@@ -616,6 +670,7 @@ def bench_cascade_arms(args, torch, pdk, W, dev):
     levels in one grid, as two launches, and with the partition sizes the
     autotuner picks for the shape bucket on a cold cache)."""
     b = W.cascade_shared_prefix()
+    args.inputs = b
     pool, csr, q = device_batch(torch, pdk, b, dev)
     arms, (part_bytes, state_bytes) = run_arms(args, torch, pdk, b, pool, q, dev, (
         ("flat", pdk.CascadeParams(enabled=0, l1_partition_tokens=512)),
@@ -659,6 +714,7 @@ def bench_nested(args, torch, pdk, W, dev):
     the sizes the autotuner picks. value = the nested arm's rate over unique
     KV bytes."""
     b = W.nested_shared_prefix()
+    args.inputs = b
     pool, csr, q = device_batch(torch, pdk, b, dev)
     base = pdk.CascadeParams(enabled=1, max_groups=0, max_depth=2)
     arms, (part_bytes, state_bytes) = run_arms(args, torch, pdk, b, pool, q, dev, (
@@ -726,6 +782,8 @@ def main():
     res = {"flat": bench_flat, "cascade": bench_cascade, "merge": bench_merge, "mla": bench_mla,
            "copy": bench_copy, "flat_mt": bench_flat_mt, "mla_mt": bench_mla_mt,
            "nested": bench_nested}[args.workload](args, torch, pdk, W, "cuda:0")
+    if not args.no_cpu_baseline and "cpu_baseline" not in res and args.workload != "copy":
+        res["cpu_baseline"] = baseline_for(args.workload, args.inputs)
     print(json.dumps(res), flush=True)
 
 
