@@ -316,10 +316,12 @@ int pdk_cascade_plan_stats(const pdk_cascade_plan* plan, int32_t stats[6], int32
  * pdk_cascade_plan_upload_device, which gathers them from csr_dev into the
  * workspace on `stream` (csr_dev must hold the same page ids then);
  * pdk_cascade_plan_upload refuses such a plan. scratch_dev: device memory
- * of pdk_cascade_device_detect_scratch_bytes(batch) bytes. One level of
- * spans only (max_depth must be 1: nested spans compare pages past a span).
- * Errors: PDK_ERR_ARG, PDK_ERR_SHAPE, PDK_ERR_WORKSPACE, PDK_ERR_UNSUPPORTED,
- * PDK_ERR_HIP. */
+ * of pdk_cascade_device_detect_scratch_bytes(batch) bytes. Nested spans
+ * (max_depth > 1) take one more detection per level of spans: each span's
+ * members are compared from the span's end page on the device (the host
+ * uploads a span key and that page offset per request, two ints per
+ * request come back), and the host applies the child-span rules.
+ * Errors: PDK_ERR_ARG, PDK_ERR_SHAPE, PDK_ERR_WORKSPACE, PDK_ERR_HIP. */
 size_t pdk_cascade_device_detect_scratch_bytes(int32_t batch);
 int pdk_cascade_plan_create_device(const pdk_csr* csr_dev, const int32_t* indptr_host,
                                    const int32_t* kv_len_host, int32_t page_size,

@@ -15,33 +15,43 @@ namespace pdk {
 
 namespace {
 
-// One wave per request b: its leader is the smallest b' <= b whose range
-// starts on the same page (64 candidates per ballot), and common[b] the
-// number of leading page ids b shares with it (64 positions per ballot).
+// One wave per request b, comparing page ids from position o = off[b]
+// (0 without offsets) among the requests of b's span key[b] (all requests
+// without keys): its leader is the smallest b' <= b with the same key and
+// offset whose page at o is b's (64 candidates per ballot), and common[b]
+// the number of page ids from o that b shares with it position by position
+// (64 per ballot). Requests with a negative offset, no page at o or no
+// token get leader -1. Without keys and offsets this is the grouping by
+// first page of the two-level plan; with them, the grouping of a span's
+// members by their page at the span's end that nested spans need.
 __global__ __launch_bounds__(64) void detect_kernel(const int32_t* __restrict__ indptr,
                                                     const int32_t* __restrict__ indices,
-                                                    const int32_t* __restrict__ kv_len, int B,
+                                                    const int32_t* __restrict__ kv_len,
+                                                    const int32_t* __restrict__ key,
+                                                    const int32_t* __restrict__ off, int B,
                                                     int32_t* __restrict__ leader,
                                                     int32_t* __restrict__ common) {
   const int b = blockIdx.x;
   const int lane = threadIdx.x;
   const int p0 = indptr[b];
   const int np = indptr[b + 1] - p0;
-  if (np < 1 || kv_len[b] < 1) {
+  const int o = off ? off[b] : 0;
+  const int k = key ? key[b] : 0;
+  if (o < 0 || np <= o || kv_len[b] < 1) {
     if (lane == 0) {
       leader[b] = -1;
       common[b] = 0;
     }
     return;
   }
-  const int first = indices[p0];
+  const int first = indices[p0 + o];
   int L = b;
   for (int base = 0; base < b; base += 64) {
     const int c = base + lane;
     bool hit = false;
-    if (c < b) {
+    if (c < b && (!key || (key[c] == k && off[c] == o))) {
       const int q0 = indptr[c];
-      hit = indptr[c + 1] - q0 >= 1 && kv_len[c] >= 1 && indices[q0] == first;
+      hit = indptr[c + 1] - q0 > o && kv_len[c] >= 1 && indices[q0 + o] == first;
     }
     const unsigned long long m = __ballot(hit);
     if (m) {
@@ -49,14 +59,14 @@ __global__ __launch_bounds__(64) void detect_kernel(const int32_t* __restrict__ 
       break;
     }
   }
-  int shared = np;
+  int shared = np - o;
   if (L != b) {
-    const int l0 = indptr[L];
-    const int n = min(np, indptr[L + 1] - l0);
+    const int l0 = indptr[L] + o;
+    const int n = min(np, indptr[L + 1] - indptr[L]) - o;
     shared = n;
     for (int base = 0; base < n; base += 64) {
       const int i = base + lane;
-      const bool diff = i < n && indices[p0 + i] != indices[l0 + i];
+      const bool diff = i < n && indices[p0 + o + i] != indices[l0 + i];
       const unsigned long long m = __ballot(diff);
       if (m) {
         shared = base + __ffsll((long long)m) - 1;
@@ -80,11 +90,14 @@ __global__ __launch_bounds__(256) void gather_pages_kernel(const int32_t* __rest
 
 }  // namespace
 
-int launch_detect(const int32_t* indptr, const int32_t* indices, const int32_t* kv_len, int B,
-                  int32_t* leader, int32_t* common, hipStream_t stream) {
+int launch_detect(const int32_t* indptr, const int32_t* indices, const int32_t* kv_len,
+                  const int32_t* key, const int32_t* off, int B, int32_t* leader,
+                  int32_t* common, hipStream_t stream) {
   if (B <= 0) return PDK_OK;
-  hipLaunchKernelGGL(detect_kernel, dim3(B), dim3(64), 0, stream, indptr, indices, kv_len, B,
-                     leader, common);
+  if ((key == nullptr) != (off == nullptr))
+    return fail(PDK_ERR_ARG, "detection keys and offsets go together");
+  hipLaunchKernelGGL(detect_kernel, dim3(B), dim3(64), 0, stream, indptr, indices, kv_len, key,
+                     off, B, leader, common);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PDK_ERR_HIP, "detect launch: %s", hipGetErrorString(e));
   return PDK_OK;

@@ -107,11 +107,14 @@ int launch_unstack(const float* v0, const float* lse0, int M, int Hkv, int G, in
                    float* v_out, float* lse_out, hipStream_t stream);
 int launch_dequant(const uint8_t* in, long long n, float scale, uint16_t* out,
                    hipStream_t stream);
-// Device detection of shared first pages: leader[b] (first request with the
-// same first page, -1 for an empty request) and common[b] (leading page ids
-// shared with the leader). The row offsets must describe [0, nnz).
-int launch_detect(const int32_t* indptr, const int32_t* indices, const int32_t* kv_len, int B,
-                  int32_t* leader, int32_t* common, hipStream_t stream);
+// Device detection of shared pages: leader[b] (first request with the same
+// page at position off[b] among those with key[b], -1 for a request without
+// that page) and common[b] (page ids from off[b] shared with the leader).
+// key and off (device [B], both or neither): without them, the first page
+// of every request. The row offsets must describe [0, nnz).
+int launch_detect(const int32_t* indptr, const int32_t* indices, const int32_t* kv_len,
+                  const int32_t* key, const int32_t* off, int B, int32_t* leader,
+                  int32_t* common, hipStream_t stream);
 // dst[segs[3i+1] + j] = src[segs[3i] + j] for j < segs[3i+2] (device arrays).
 int launch_gather_pages(const int32_t* src, const int32_t* segs, int nseg, int32_t* dst,
                         hipStream_t stream);

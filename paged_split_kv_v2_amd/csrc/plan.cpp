@@ -36,6 +36,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <functional>
 #include <map>
 #include <vector>
 
@@ -153,9 +154,19 @@ int check_params(const pdk_cascade_params& pr, int32_t P) {
 // and nested spans, which compare pages past a span, are not available.
 static int upload_blob(pdk_cascade_plan* plan, void* ws, size_t ws_bytes, hipStream_t stream);
 
+// Device detection below a level of spans: for every request b with
+// key[b] >= 0 (its span at that level) and off[b] (the span's end page),
+// leader[b] is the first request of the same span with the same page at
+// off[b] (-1: none) and common[b] the page ids from off[b] it shares with
+// that leader, position by position.
+typedef std::function<int(const std::vector<int32_t>& key, const std::vector<int32_t>& off,
+                          std::vector<int32_t>& leader, std::vector<int32_t>& common)>
+    DetectBelow;
+
 static int build_plan(int B, int32_t P, const pdk_cascade_params& pr, const int32_t* indptr,
                const int32_t* len, const int32_t* idx, const std::vector<int32_t>& leader,
-               const std::vector<int32_t>& common, pdk_cascade_plan** plan_out) {
+               const std::vector<int32_t>& common, pdk_cascade_plan** plan_out,
+               const DetectBelow& detect_below = nullptr) {
   auto plan = new pdk_cascade_plan();
   plan->batch = B;
   plan->page_size = P;
@@ -223,27 +234,55 @@ static int build_plan(int B, int32_t P, const pdk_cascade_params& pr, const int3
   for (const auto& c : chosen) nodes.push_back({c.members, 0, c.span, 0, -1});
   {
     size_t lo = 0, hi = nodes.size();
-    for (int depth = 1; depth < pr.max_depth && idx && lo < hi; ++depth) {
+    for (int depth = 1; depth < pr.max_depth && (idx || detect_below) && lo < hi; ++depth) {
       std::vector<SpanNode> next;
+      // without host page ids: the members' pages at each span's end,
+      // grouped and compared on the device
+      std::vector<int32_t> lead2, common2;
+      if (!idx) {
+        std::vector<int32_t> key(B, -1), off(B, -1);
+        for (size_t i = lo; i < hi; ++i)
+          for (int32_t b : nodes[i].members) {
+            key[b] = (int32_t)i;
+            off[b] = nodes[i].start + nodes[i].span;
+          }
+        const int st = detect_below(key, off, lead2, common2);
+        if (st) {
+          delete plan;
+          return st;
+        }
+      }
       for (size_t i = lo; i < hi; ++i) {
         const int32_t e = nodes[i].start + nodes[i].span;
+        // subgroups by the page at e (keyed by page id, or by the subgroup's
+        // first member when the device compared them), members ascending
         std::map<int32_t, std::vector<int32_t>> by_page;
-        for (int32_t b : nodes[i].members)
-          if (indptr[b + 1] - indptr[b] > e) by_page[idx[indptr[b] + e]].push_back(b);
+        for (int32_t b : nodes[i].members) {
+          if (indptr[b + 1] - indptr[b] <= e) continue;
+          if (idx) by_page[idx[indptr[b] + e]].push_back(b);
+          else if (lead2[b] >= 0) by_page[lead2[b]].push_back(b);
+        }
         for (auto& kv : by_page) {
           const auto& mem = kv.second;  // ascending batch order
           if ((int)mem.size() < std::max(2, pr.min_members)) continue;
+          // positional common prefix from e of all members
           int32_t c = 0;
-          for (;;) {
-            bool ok = true;
-            for (int32_t b : mem)
-              if (e + c >= indptr[b + 1] - indptr[b] ||
-                  idx[indptr[b] + e + c] != idx[indptr[mem[0]] + e + c]) {
-                ok = false;
-                break;
-              }
-            if (!ok) break;
-            ++c;
+          if (idx) {
+            for (;;) {
+              bool ok = true;
+              for (int32_t b : mem)
+                if (e + c >= indptr[b + 1] - indptr[b] ||
+                    idx[indptr[b] + e + c] != idx[indptr[mem[0]] + e + c]) {
+                  ok = false;
+                  break;
+                }
+              if (!ok) break;
+              ++c;
+            }
+          } else {
+            // every member's prefix shared with the subgroup's first member
+            c = common2[mem[0]];
+            for (int32_t b : mem) c = std::min(c, common2[b]);
           }
           for (int32_t b : mem) c = std::min(c, len[b] / P - e);
           if (c < std::max(1, pr.min_shared_pages)) continue;
@@ -436,7 +475,7 @@ int pdk_cascade_plan_create(const pdk_csr* csr, int32_t P, const pdk_cascade_par
 
 size_t pdk_cascade_device_detect_scratch_bytes(int32_t batch) {
   if (batch < 0) return 0;
-  return align256(2 * (size_t)std::max(batch, 1) * sizeof(int32_t));
+  return align256(4 * (size_t)std::max(batch, 1) * sizeof(int32_t));
 }
 
 int pdk_cascade_plan_create_device(const pdk_csr* csr_dev, const int32_t* indptr_host,
@@ -452,8 +491,6 @@ int pdk_cascade_plan_create_device(const pdk_csr* csr_dev, const int32_t* indptr
   if (P <= 0) return fail(PDK_ERR_ARG, "page_size %d", P);
   int st = check_params(*params, P);
   if (st) return st;
-  if (params->max_depth != 1)
-    return fail(PDK_ERR_UNSUPPORTED, "device detection finds one level of spans (max_depth 1)");
   // the host copies of the row offsets and lengths must describe the device
   // table: every page-id read of the kernels stays inside [0, nnz)
   if (indptr_host[0] != 0 || indptr_host[B] > csr_dev->nnz)
@@ -466,26 +503,51 @@ int pdk_cascade_plan_create_device(const pdk_csr* csr_dev, const int32_t* indptr
                   kv_len_host[b], P);
   }
   std::vector<int32_t> leader(B, -1), common(B, 0);
-  if (B > 0 && params->enabled == 1) {
-    if (!csr_dev->indptr || !csr_dev->kv_len || (csr_dev->nnz > 0 && !csr_dev->indices))
-      return fail(PDK_ERR_ARG, "NULL device page table");
-    if (!scratch || scratch_bytes < pdk_cascade_device_detect_scratch_bytes(B))
-      return fail(PDK_ERR_WORKSPACE, "detection scratch %zu bytes < %zu", scratch_bytes,
-                  pdk_cascade_device_detect_scratch_bytes(B));
-    // leader[B] then common[B], read back with one copy
-    int32_t* d_out = (int32_t*)scratch;
-    if ((st = launch_detect(csr_dev->indptr, csr_dev->indices, csr_dev->kv_len, B, d_out,
-                            d_out + B, stream)))
-      return st;
+  if (B == 0 || params->enabled != 1)
+    return build_plan(B, P, *params, indptr_host, kv_len_host, nullptr, leader, common,
+                      plan_out);
+  if (!csr_dev->indptr || !csr_dev->kv_len || (csr_dev->nnz > 0 && !csr_dev->indices))
+    return fail(PDK_ERR_ARG, "NULL device page table");
+  if (!scratch || scratch_bytes < pdk_cascade_device_detect_scratch_bytes(B))
+    return fail(PDK_ERR_WORKSPACE, "detection scratch %zu bytes < %zu", scratch_bytes,
+                pdk_cascade_device_detect_scratch_bytes(B));
+  // scratch: leader[B], common[B] (read back with one copy), then the keys
+  // and offsets of a level of spans
+  int32_t* d_out = (int32_t*)scratch;
+  int32_t* d_key = d_out + 2 * (size_t)B;
+  int32_t* d_off = d_key + B;
+  auto detect = [&](const std::vector<int32_t>* key, const std::vector<int32_t>* off,
+                    std::vector<int32_t>& lead, std::vector<int32_t>& comm) {
+    hipError_t e = hipSuccess;
+    if (key) {
+      e = hipMemcpyAsync(d_key, key->data(), B * sizeof(int32_t), hipMemcpyHostToDevice, stream);
+      if (e == hipSuccess)
+        e = hipMemcpyAsync(d_off, off->data(), B * sizeof(int32_t), hipMemcpyHostToDevice,
+                           stream);
+      if (e != hipSuccess) return fail(PDK_ERR_HIP, "detection upload: %s", hipGetErrorString(e));
+    }
+    int rc = launch_detect(csr_dev->indptr, csr_dev->indices, csr_dev->kv_len,
+                           key ? d_key : nullptr, key ? d_off : nullptr, B, d_out, d_out + B,
+                           stream);
+    if (rc) return rc;
     std::vector<int32_t> both(2 * (size_t)B);
-    hipError_t e = hipMemcpyAsync(both.data(), d_out, both.size() * sizeof(int32_t),
-                                  hipMemcpyDeviceToHost, stream);
+    e = hipMemcpyAsync(both.data(), d_out, both.size() * sizeof(int32_t), hipMemcpyDeviceToHost,
+                       stream);
+    // also orders the key/offset uploads before their host buffers go away
     if (e == hipSuccess) e = hipStreamSynchronize(stream);
     if (e != hipSuccess) return fail(PDK_ERR_HIP, "detection readback: %s", hipGetErrorString(e));
-    leader.assign(both.begin(), both.begin() + B);
-    common.assign(both.begin() + B, both.end());
-  }
-  return build_plan(B, P, *params, indptr_host, kv_len_host, nullptr, leader, common, plan_out);
+    lead.assign(both.begin(), both.begin() + B);
+    comm.assign(both.begin() + B, both.end());
+    return (int)PDK_OK;
+  };
+  if ((st = detect(nullptr, nullptr, leader, common))) return st;
+  // nested spans: one more detection per level below the outermost spans
+  const DetectBelow below = [&](const std::vector<int32_t>& key, const std::vector<int32_t>& off,
+                                std::vector<int32_t>& lead, std::vector<int32_t>& comm) {
+    return detect(&key, &off, lead, comm);
+  };
+  return build_plan(B, P, *params, indptr_host, kv_len_host, nullptr, leader, common, plan_out,
+                    below);
 }
 
 int pdk_cascade_plan_upload_device(pdk_cascade_plan* plan, const pdk_csr* csr_dev, void* ws,

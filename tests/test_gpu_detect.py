@@ -1,10 +1,10 @@
 """Shared-prefix detection on the device (page ids only on the GPU) against
 the host planner [cascade-PR, "Detection reads the page table, not the
 refcounts"]: every plan field, the stats and the decline reason equal the
-host plan's for the same table; the views' page ids, gathered on the device
-at upload, give bit-identical decode outputs; tables with thousands of
-requests (the grouping scan crosses many 64-request chunks) and every
-rejection case; misuse is refused."""
+host plan's for the same table, nested spans included; the views' page ids,
+gathered on the device at upload, give bit-identical decode outputs; tables
+with thousands of requests (the grouping scan crosses many 64-request
+chunks) and every rejection case; misuse is refused."""
 import numpy as np
 import pytest
 import torch
@@ -89,9 +89,6 @@ def test_misuse_is_refused(gpu):
     b = W.cascade_shared_prefix(seed=2630, groups=2, members=4, prefix_tokens=512,
                                 suffix_max=200, extra=1, extra_tokens=300)
     csr = gpu.DeviceCSR.from_host(b.indptr, b.indices, b.kv_len)
-    with pytest.raises(gpu.PdkError):     # nested spans need host page ids
-        gpu.CascadePlan.from_device(csr, b.indptr, b.kv_len, 16,
-                                    gpu.CascadeParams(enabled=1, max_depth=2))
     bad = b.kv_len.copy()
     bad[0] += 64                          # 4 more pages than the table holds
     with pytest.raises(gpu.PdkError):
@@ -101,3 +98,63 @@ def test_misuse_is_refused(gpu):
     ws = torch.empty(dev.workspace_bytes(32, 128), dtype=torch.uint8, device="cuda")
     # the plain upload would leave the views' page ids unset
     assert gpu.lib().pdk_cascade_plan_upload(dev._h, ws.data_ptr(), ws.numel(), None) != 0
+
+
+def random_nested_table(rng, B, P=16):
+    """Requests walking down a random forest of shared page runs (root run,
+    then one of its child runs, then a grandchild run), then private pages."""
+    nxt = 0
+    def run(n):
+        nonlocal nxt
+        r = list(range(nxt, nxt + n))
+        nxt += n
+        return r
+    roots = [run(int(rng.integers(1, 5))) for _ in range(3)]
+    kids = [[run(int(rng.integers(1, 4))) for _ in range(int(rng.integers(1, 4)))]
+            for _ in roots]
+    grand = [[[run(int(rng.integers(1, 3))) for _ in range(2)] for _ in k] for k in kids]
+    lists = []
+    for _ in range(B):
+        i = int(rng.integers(0, len(roots)))
+        pl = list(roots[i])
+        if rng.random() < 0.85:
+            j = int(rng.integers(0, len(kids[i])))
+            pl += kids[i][j]
+            if rng.random() < 0.7:
+                pl += grand[i][j][int(rng.integers(0, 2))]
+        pl += run(int(rng.integers(0, 4)))
+        lists.append(pl)
+    kv = [len(pl) * P - int(rng.integers(0, P)) for pl in lists]
+    indptr = np.cumsum([0] + [len(pl) for pl in lists]).astype(np.int32)
+    indices = np.asarray([p for pl in lists for p in pl], np.int32)
+    return indptr, indices, np.asarray(kv, np.int32)
+
+
+@pytest.mark.parametrize("max_depth", [2, 3, 4])
+def test_device_nested_plans_equal_host_plans(gpu, max_depth):
+    rng = np.random.default_rng(2640 + max_depth)
+    deep = 0
+    for B in (6, 40, 300):
+        for _ in range(6):
+            ip, ix, kl = random_nested_table(rng, B)
+            params = gpu.CascadeParams(enabled=1, max_groups=0, min_shared_pages=1,
+                                       max_depth=max_depth, l0_partition_tokens=64,
+                                       l1_partition_tokens=128)
+            host, _ = both(gpu, ip, ix, kl, 16, params)
+            deep += int((host.field("span_parent") >= 0).sum())
+    assert deep > 0    # the tables do produce nested spans
+
+
+def test_device_nested_plan_runs_bit_identical(gpu):
+    b = W.nested_shared_prefix(seed=2650, tenants=3, members=5, system_tokens=512,
+                               tenant_tokens=256, suffix_min=1, suffix_max=200, extra=2,
+                               extra_tokens=300)
+    pool, csr, q = to_device(b)
+    params = gpu.CascadeParams(enabled=1, max_groups=0, max_depth=2, l0_partition_tokens=256,
+                               l1_partition_tokens=256)
+    host, dev = both(gpu, b.indptr, b.indices, b.kv_len, b.page_size, params)
+    assert len(host.field("span_pages")) == 4     # system prompt + 3 tenant spans
+    ho, hl = host.run(pool, q, b.sm_scale)
+    do, dl = dev.run(pool, q, b.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(ho, do) and torch.equal(hl, dl)
