@@ -726,6 +726,10 @@ def bench_nested(args, torch, pdk, W, dev):
         ("nested_spans_autotuned", None)), tune_base=base, bytes_arm="nested_spans")
     best = arms["nested_spans"]
     kv = b.unique_kv_bytes()
+    # planning from a device page table: one detection per level of spans
+    planning = planning_with_device_table_us(
+        torch, pdk, b, csr, pdk.CascadeParams(enabled=1, max_groups=0, max_depth=2,
+                                              l0_partition_tokens=1024, l1_partition_tokens=512))
     achieved = part_bytes / (best["partials_us"] * 1e-6) / 1e9
     return {"metric": METRIC, "value": best["unique_kv_GBps"], "unit": "GB/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup,
@@ -749,6 +753,7 @@ def bench_nested(args, torch, pdk, W, dev):
                          "bytes_per_launch": part_bytes},
             "partial_state_bytes": state_bytes, "unique_kv_bytes": kv,
             "flat_read_bytes": b.read_kv_bytes(), "arms": arms,
+            "device_page_table_planning": planning,
             "speedup_nested_vs_flat": round(arms["flat"]["us_per_step"] /
                                             best["us_per_step"], 3),
             "speedup_nested_vs_one_level": round(arms["one_span_level"]["us_per_step"] /
