@@ -15,7 +15,8 @@
 // waves of a workgroup take independent (output row, 256-float span) units.
 // (Measured on 8192 output rows of 32 x 128 floats, 1-16 rows per group:
 // sixteen rows per round trip 228 us against 243 us for eight, 219 us with
-// non-temporal loads and stores; issuing the loads from scalar row bases cuts
+// non-temporal loads and stores, 208 us with the group bounds read through
+// the scalar cache; issuing the loads from scalar row bases cuts
 // registers to four waves per SIMD but runs slower, 235 us, and so does a
 // grid-stride loop over units, 269 us.)
 
@@ -43,7 +44,10 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
     const float* __restrict__ v_in, const float* __restrict__ lse_in, int num_in,
     const int* __restrict__ o_indptr, int H, int D, int chunks, long long units,
     int out_stride, float* __restrict__ v_out, float* __restrict__ lse_out) {
-  const long long unit = (long long)blockIdx.x * (kMergeThreads / 64) + (threadIdx.x >> 6);
+  // the wave's unit, known wave-uniform: its group bounds come through the
+  // scalar cache
+  const long long unit = (long long)blockIdx.x * (kMergeThreads / 64) +
+                         __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (unit >= units) return;  // no barrier below
   const int i = (int)(unit / chunks);
   const int c = (int)(unit - (long long)i * chunks);
