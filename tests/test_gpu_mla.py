@@ -104,3 +104,26 @@ def test_mla_ragged_and_empty_suffix(gpu):
     assert_close(out, fo, TOL["fp8_e4m3"], "out vs one softmax")
     o1, l1, _, _, _ = run_chunked(gpu, share, staged=False)
     assert_close(o1, out, 1e-5, "single merge vs staged")
+
+
+def test_mla_partitions_of_every_tile_count_mod_three(gpu):
+    """Partitions of 3, 5, 6 and 9 tiles of 32 tokens (and a suffix of 3, 4, 2
+    and 1 tiles): the latent kernel cycles three tile buffers, and half of its
+    waves apply a tile's PV product one tile late, so the last tile of a
+    partition sits in each of the three buffers across these cases."""
+    pre_lens, suf_lens = [96, 150, 190, 288], [96, 0, 190, 32]
+    pre = W.random_batch(3111, batch=4, page_size=64, num_q_heads=128, num_kv_heads=1,
+                         head_dim=576, head_dim_v=512, kv_dtype="fp8_e4m3", q_dtype="bf16",
+                         min_len=0, max_len=0, partition_tokens=512, lens=pre_lens, latent=True)
+    suf = W.random_batch(3112, batch=4, page_size=64, num_q_heads=128, num_kv_heads=1,
+                         head_dim=576, head_dim_v=512, kv_dtype="bf16", q_dtype="bf16",
+                         min_len=0, max_len=0, partition_tokens=128, lens=suf_lens, latent=True)
+    suf.q = pre.q
+    suf.sm_scale = pre.sm_scale
+    share = W.MlaShare(prefix=pre, suffix=suf, chunk_tokens=512)
+    out, lse, cout, clse, counts = run_chunked(gpu, share)
+    ro, rl, rco, rcl = omla.mla_decode(share)
+    assert_close(cout, rco, TOL["fp8_e4m3"], "chunk out")
+    assert_lse(clse, rcl, "chunk lse")
+    assert_close(out, ro, TOL["fp8_e4m3"], "out")
+    assert_lse(lse, rl, "lse")
