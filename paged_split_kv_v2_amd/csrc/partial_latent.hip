@@ -65,10 +65,6 @@ constexpr bool kStagger = true;  // second half of the waves one PV product behi
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t w) { return __builtin_bit_cast(bf16x8_t, w); }
 
-__device__ __forceinline__ u32x4_t ld_nt16(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-}
-
 // Stored position of 16-byte chunk q of token row t. The swizzle permutes
 // chunks within aligned groups of 8: rows of equal parity get distinct
 // positions for 16 consecutive tokens (16-byte loads of one chunk), and rows
