@@ -228,22 +228,6 @@ def build_cascade_plan(indptr, indices, kv_len, page_size, params: CascadeParams
     return plan
 
 
-def fused_merge_indptr(plan: CascadePlan, params: CascadeParams) -> np.ndarray:
-    """Rows per request when each request's level-0 partitions (members only)
-    and level-1 partitions (at least one, possibly empty) sit contiguously and
-    one merge combines them all.
-    Legal because the merge is associative across regroupings [cascade-PR,
-    "How the #898 merge kernel is reused"]."""
-    S0, S1 = int(params.l0_partition_tokens), int(params.l1_partition_tokens)
-    out = [0]
-    for b in range(plan.batch):
-        k = int(plan.group_of[b])
-        n0 = _ceil_div(int(plan.l0_len[k]), S0) if k >= 0 else 0
-        # an empty level-1 range still contributes its (0, -inf) state row
-        out.append(out[-1] + n0 + max(1, _ceil_div(int(plan.l1_len[b]), S1)))
-    return np.asarray(out, dtype=np.int32)
-
-
 def stacked_head_map(num_members: int, num_kv_heads: int, group: int) -> np.ndarray:
     """KV-head-major stacking [cascade-PR, "The decomposition, and the one
     part that is not obvious"]: stacked head h0 = kv*(M*G) + m*G + g holds

@@ -42,7 +42,6 @@ def test_tiny_plan_matches_hand_worked_golden():
     assert plan.l1_len.tolist() == g["l1_len"]
     assert np.diff(plan.l1_indptr).tolist() == g["l1_pages"]
     assert plan.merge_indptr.tolist() == g["merge_indptr"]
-    assert planner.fused_merge_indptr(plan, params).tolist() == g["fused_merge_indptr"]
     assert plan.stats == g["stats"]
     assert plan.l0_indices.tolist() == b.indices[:2].tolist()
 

@@ -12,6 +12,38 @@ FIELDS = ["members", "group_indptr", "span_pages", "l0_indptr", "l0_indices", "l
           "l1_indptr", "l1_indices", "l1_len", "merge_indptr", "group_of", "member_rank"]
 
 
+def fused_rows(group_of, l0_len, l1_len, params):
+    """The library's single-merge row layout, written out from its reading
+    (not a rule of the page, which pairs one level-0 and one level-1 state
+    per member): request b owns ceil(l0_len/S0) rows for the span holding it
+    (none for a non-member), then max(1, ceil(l1_len/S1)) level-1 rows, so an
+    empty level-1 range still owns the (0, -inf) row its merge reads."""
+    S0, S1 = int(params.l0_partition_tokens), int(params.l1_partition_tokens)
+    out = [0]
+    for b in range(len(l1_len)):
+        k = int(group_of[b])
+        n0 = -(-int(l0_len[k]) // S0) if k >= 0 else 0
+        out.append(out[-1] + n0 + max(1, -(-int(l1_len[b]) // S1)))
+    return np.asarray(out, dtype=np.int32)
+
+
+def test_fused_rows_with_an_empty_level1_range():
+    """Worked by hand: the tiny workload's batch (requests 0-2 share two
+    pages and own 1/2/3 private pages, request 3 owns 4 pages, page 16) plus
+    a fifth request of length 0, partitions of 32 tokens. Members own one
+    level-0 row each (32 shared tokens) and 1/1/2 level-1 rows (16/32/48
+    tokens); request 3 owns 2 level-1 rows; request 4's empty range owns one
+    row."""
+    b = tiny_gqa_fp32()
+    indptr = np.concatenate([b.indptr, b.indptr[-1:]]).astype(np.int32)
+    kv_len = np.concatenate([b.kv_len, [0]]).astype(np.int32)
+    kw = dict(enabled=1, min_shared_pages=2, l0_partition_tokens=32, l1_partition_tokens=32)
+    plan, ref = compare(indptr, b.indices, kv_len, 16, **kw)
+    assert ref.l1_len.tolist() == [16, 32, 48, 64, 0]
+    assert plan.field("fused_merge_indptr").tolist() == [0, 2, 4, 7, 9, 10]
+    assert plan.field("merge_indptr").tolist() == [0, 2, 4, 6, 7, 8]
+
+
 def compare(indptr, indices, kv_len, P, **kw):
     op = oplan.CascadeParams(**kw)
     ref = oplan.build_cascade_plan(indptr, indices, kv_len, P, op)
@@ -20,7 +52,8 @@ def compare(indptr, indices, kv_len, P, **kw):
         want = np.asarray(getattr(ref, f), dtype=np.int64)
         got = plan.field(f).astype(np.int64)
         assert np.array_equal(got, want), f
-    assert np.array_equal(plan.field("fused_merge_indptr"), oplan.fused_merge_indptr(ref, op))
+    assert np.array_equal(plan.field("fused_merge_indptr"),
+                          fused_rows(ref.group_of, ref.l0_len, ref.l1_len, op))
     stats, decline = plan.stats()
     assert stats == ref.stats
     assert decline == ref.decline
@@ -143,6 +176,14 @@ def test_nested_plans_match_the_oracle(depth):
         plan = pdk.CascadePlan(indptr, indices, kv_len, P, pdk.CascadeParams(max_depth=depth, **kw))
         for f, v in want.items():
             assert np.array_equal(plan.field(f).astype(np.int64), np.asarray(v, np.int64)), f
+        # single-merge layout: every span holding the request, then its
+        # level-1 rows (at least one)
+        S0, S1 = kw["l0_partition_tokens"], kw["l1_partition_tokens"]
+        rows = [0]
+        for b, n1 in enumerate(want["l1_len"]):
+            n0 = sum(-(-ref.spans[k].span_pages * P // S0) for k in ref.spans_of[b])
+            rows.append(rows[-1] + n0 + max(1, -(-int(n1) // S1)))
+        assert plan.field("fused_merge_indptr").tolist() == rows
         stats, decline = plan.stats()
         S0, S1 = kw["l0_partition_tokens"], kw["l1_partition_tokens"]
         assert decline == ref.decline
