@@ -30,9 +30,13 @@
  *   - Page table: CSR indptr[batch+1], indices[indptr[batch]] (pool rows),
  *     kv_len[batch] (tokens). Token t of request b lives in slot t % P of row
  *     indices[indptr[b] + t / P]; indptr[b+1] - indptr[b] == ceil(kv_len[b]/P).
- *     Kernels never read a row outside [0, num_blocks) nor a token at or past
- *     kv_len[b]; a malformed device CSR gives wrong numbers but no fault.
- *     pdk_validate_csr checks a host copy.
+ *     Kernels never read a page id outside [0, nnz), a pool row outside
+ *     [0, num_blocks) nor a token at or past kv_len[b]: a request's page-id
+ *     offsets are clamped to [0, nnz) and its range to the pages it has, and
+ *     a page id outside [0, num_blocks) is read as pool row 0 on every
+ *     kernel path. A malformed device CSR therefore gives wrong numbers for
+ *     the requests it touches, never a fault. pdk_validate_csr checks a host
+ *     copy.
  *   - Query: one token per request, q [batch, num_q_heads, head_dim_k] in f32
  *     or bf16, row major. Query head i reads KV head i / (Hq / Hkv)
  *     [cascade-PR, "The decomposition, and the one part that is not obvious"].

@@ -158,7 +158,8 @@ def _stream(stream=None):
 def _ptr(t: Optional[torch.Tensor]):
     if t is None:
         return None
-    assert t.is_contiguous(), "tensors passed to pdk must be contiguous"
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to pdk must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
 
 
@@ -200,6 +201,22 @@ class KVPool:
         return int(self.k.shape[1])
 
     def struct(self) -> _Pool:
+        """The C struct; the pool tensors must be contiguous HND
+        [num_blocks, Hkv, P, D] (a strided view such as cache[:, 0] of a
+        [N, 2, Hkv, P, D] tensor would be read with the wrong strides)."""
+        k, v = self.k, self.v
+        if k.dim() != 4 or not k.is_contiguous():
+            raise ValueError(f"pool k must be a contiguous 4-D [num_blocks, Hkv, P, D] tensor "
+                             f"(got shape {tuple(k.shape)}, contiguous={k.is_contiguous()})")
+        if v is not None:
+            if v.dim() != 4 or not v.is_contiguous():
+                raise ValueError("pool v must be a contiguous 4-D [num_blocks, Hkv, P, Dv] "
+                                 f"tensor (got shape {tuple(v.shape)})")
+            if tuple(v.shape[:3]) != tuple(k.shape[:3]) or int(v.shape[3]) != int(self.head_dim_v):
+                raise ValueError(f"pool v shape {tuple(v.shape)} does not match k "
+                                 f"{tuple(k.shape)} and head_dim_v {self.head_dim_v}")
+            if v.dtype != k.dtype:
+                raise ValueError(f"pool k and v dtypes differ ({k.dtype}, {v.dtype})")
         return _Pool(self.k.data_ptr(), None if self.v is None else self.v.data_ptr(),
                      int(self.k.shape[0]), int(self.k.shape[2]), int(self.k.shape[1]),
                      int(self.k.shape[3]), int(self.head_dim_v), _dtype_code(self.k),
@@ -225,6 +242,16 @@ class DeviceCSR:
         return int(self.kv_len.shape[0])
 
     def struct(self) -> _CSR:
+        """The C struct; indptr [batch+1], indices [nnz] and kv_len [batch]
+        must be contiguous 1-D int32 tensors (an int64 table would be read
+        as twice as many int32 words)."""
+        for name in ("indptr", "indices", "kv_len"):
+            t = getattr(self, name)
+            if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous():
+                raise ValueError(f"page table {name} must be a contiguous 1-D int32 tensor "
+                                 f"(got {t.dtype}, shape {tuple(t.shape)})")
+        if int(self.indptr.numel()) != self.batch + 1:
+            raise ValueError(f"indptr has {self.indptr.numel()} entries for batch {self.batch}")
         return _CSR(self.indptr.data_ptr(), self.indices.data_ptr(), self.kv_len.data_ptr(),
                     self.batch, int(self.indices.numel()))
 

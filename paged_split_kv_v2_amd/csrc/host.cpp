@@ -101,7 +101,8 @@ int partial_args(const pdk_kv_pool* pool, const pdk_csr* csr, const void* q, int
   int st = check_pool(pool);
   if (st) return st;
   if ((st = check_query(q, q_dtype, Hq, pool))) return st;
-  if (!csr || csr->batch < 0) return fail(PDK_ERR_ARG, "csr is NULL or batch < 0");
+  if (!csr || csr->batch < 0 || csr->nnz < 0)
+    return fail(PDK_ERR_ARG, "csr is NULL, batch < 0 or nnz < 0");
   if (S <= 0 || S % pool->page_size != 0)
     return fail(PDK_ERR_ARG, "partition_tokens %d must be a positive multiple of page_size %d", S,
                 pool->page_size);
@@ -123,6 +124,7 @@ int partial_args(const pdk_kv_pool* pool, const pdk_csr* csr, const void* q, int
   a.indices = csr->indices;
   a.kv_len = csr->kv_len;
   a.batch = csr->batch;
+  a.nnz = csr->nnz;
   a.part_indptr = part_indptr;
   a.num_parts = num_parts;
   a.S = S;

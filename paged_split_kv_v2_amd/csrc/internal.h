@@ -34,6 +34,7 @@ struct PartialArgs {
   const int* indices;
   const int* kv_len;
   int batch;
+  int nnz;                    // page ids in indices; every read is clamped to [0, nnz)
   const int* part_indptr;     // [batch+1] partitions of the view
   int num_parts;
   int S;                      // partition tokens

@@ -118,11 +118,8 @@ __device__ __forceinline__ void partial_dma_body(const PartialArgs& a, const int
   const int row0 = rt * 16 * NW;
   if (row0 >= nrows) return;  // uniform
 
-  const int page0 = a.indptr[b];
-  const int npages = a.indptr[b + 1] - page0;
-  const int start = p * a.S;
-  int end = min(start + a.S, a.kv_len[b]);
-  end = min(end, npages * a.P);
+  int page0, start, end;
+  part_range(a, b, p, page0, start, end);
   // causal rows: the tile loop stops at the last owned row's end; every
   // owned row sees at least the positions below end_lo (uniform)
   const int end_lo = min(end, visible_end(a, b, row0 / a.G));
@@ -134,7 +131,7 @@ __device__ __forceinline__ void partial_dma_body(const PartialArgs& a, const int
     const int n_pg = ((end - 1) >> shift) - pg_first + 1;
     for (int i = tid; i < n_pg; i += 64 * NW) {
       const int pid = a.indices[page0 + pg_first + i];
-      // an id outside the pool reads row 0: wrong numbers, never a fault
+      // an id outside the pool reads row 0 (see part_range)
       sm_pid[i] = ((unsigned)pid < (unsigned)a.num_blocks) ? pid : 0;
     }
   }

@@ -119,11 +119,8 @@ __global__ __launch_bounds__(64 * NW) void partial_mfma_kernel(const PartialArgs
   const int row0 = tile * 16 * NW;
   if (row0 >= nrows) return;  // uniform
 
-  const int page0 = a.indptr[b];
-  const int npages = a.indptr[b + 1] - page0;
-  const int start = p * a.S;
-  int end = min(start + a.S, a.kv_len[b]);
-  end = min(end, npages * a.P);
+  int page0, start, end;
+  part_range(a, b, p, page0, start, end);
   // causal rows: the tile loop stops at the last owned row's end
   end = min(end, visible_end(a, b, (min(row0 + 16 * NW, nrows) - 1) / a.G));
   const int shift = a.p_shift;
@@ -133,7 +130,7 @@ __global__ __launch_bounds__(64 * NW) void partial_mfma_kernel(const PartialArgs
     const int n_pg = ((end - 1) >> shift) - pg_first + 1;
     for (int i = tid; i < n_pg; i += NT) {
       const int pid = a.indices[page0 + pg_first + i];
-      // an id outside the pool reads row 0: wrong numbers, never a fault
+      // an id outside the pool reads row 0 (see part_range)
       sm_pid[i] = ((unsigned)pid < (unsigned)a.num_blocks) ? pid : 0;
     }
   }

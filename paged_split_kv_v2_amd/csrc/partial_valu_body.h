@@ -328,11 +328,8 @@ __device__ __forceinline__ void partial_valu_body(const PartialArgs& a, const in
   const int row0 = tile * GM;
   if (row0 >= nrows) return;  // uniform over the workgroup
 
-  const int page0 = a.indptr[b];
-  const int npages = a.indptr[b + 1] - page0;
-  const int start = p * a.S;
-  int end = min(start + a.S, a.kv_len[b]);
-  end = min(end, npages * a.P);
+  int page0, start, end;
+  part_range(a, b, p, page0, start, end);
   // causal rows: positions past the last owned row's end are never read
   int lim[GM];
 #pragma unroll
@@ -347,13 +344,14 @@ __device__ __forceinline__ void partial_valu_body(const PartialArgs& a, const in
   const int rg = tid >> 4;
   const int j = tid & 15;
 
-  // stage the partition's page ids (-1 marks an id outside the pool)
+  // stage the partition's page ids (an id outside the pool reads row 0, as
+  // on every path; see part_range)
   const int pg_first = start >> shift;
   if (end > start) {
     const int n_pg = ((end - 1) >> shift) - pg_first + 1;
     for (int i = tid; i < n_pg; i += kThreads) {
       const int pid = a.indices[page0 + pg_first + i];
-      sm_pid[i] = ((unsigned)pid < (unsigned)a.num_blocks) ? pid : -1;
+      sm_pid[i] = ((unsigned)pid < (unsigned)a.num_blocks) ? pid : 0;
     }
   }
 
@@ -417,9 +415,8 @@ __device__ __forceinline__ void partial_valu_body(const PartialArgs& a, const in
       // with pages of >= 16 tokens, the 4 tokens a wave takes for one u lie
       // in one page: its row base is wave-uniform (scalar address)
       if constexpr (UNIF) pid = __builtin_amdgcn_readfirstlane(pid);
-      X.valid[u] = (t < end) && (pid >= 0);
+      X.valid[u] = t < end;
       X.tok[u] = t;
-      pid = max(pid, 0);
       const uint32_t slot = (uint32_t)(tc & pmask);
       const char* kp = kbase + pid * kb_stride;
       const char* vp = vbase + pid * vb_stride;

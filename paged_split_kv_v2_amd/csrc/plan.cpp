@@ -634,7 +634,8 @@ int pdk_run_cascade_partials(const pdk_cascade_plan* plan, const pdk_kv_pool* po
   PartialArgs a0{}, a1{};
   bool empty0 = true, empty1 = true;
   if (plan->n_l0_parts > 0) {
-    pdk_csr v0{base + o.l0_indptr, base + o.l0_indices, base + o.l0_len, plan->n_groups, 0};
+    pdk_csr v0{base + o.l0_indptr, base + o.l0_indices, base + o.l0_len, plan->n_groups,
+               plan->f[PDK_PLAN_L0_INDPTR].back()};
     int st = partial_args(pool, &v0, q, q_dtype, Hq, sm_scale, plan->params.l0_partition_tokens,
                           base + o.l0_parts, plan->n_l0_parts, base + o.group_indptr,
                           base + o.members, plan->max_members, G, base + o.member_rows, v_part,
@@ -642,7 +643,8 @@ int pdk_run_cascade_partials(const pdk_cascade_plan* plan, const pdk_kv_pool* po
     if (st) return st;
   }
   // level 1: every request's remaining range (the flat batch when declined)
-  pdk_csr v1{base + o.l1_indptr, base + o.l1_indices, base + o.l1_len, plan->batch, 0};
+  pdk_csr v1{base + o.l1_indptr, base + o.l1_indices, base + o.l1_len, plan->batch,
+             plan->f[PDK_PLAN_L1_INDPTR].back()};
   int st = partial_args(pool, &v1, q, q_dtype, Hq, sm_scale, plan->params.l1_partition_tokens,
                         base + o.l1_parts, plan->n_l1_parts, nullptr, nullptr, 0, G,
                         base + o.l1_rows, v_part, lse_part,
@@ -691,6 +693,7 @@ int pdk_run_cascade_decode(const pdk_cascade_plan* plan, const pdk_kv_pool* pool
 
 struct pdk_chunked_plan {
   int32_t batch = 0, n_chunks = 0, n_pre_parts = 0, n_suf_parts = 0;
+  int32_t ch_nnz = 0, suf_nnz = 0;  // page ids of the chunk and suffix views
   int32_t P = 0, C = 0, S = 0, Ps = 0, Ss = 0;
   Blob blob;
   struct {
@@ -779,6 +782,8 @@ int pdk_chunked_plan_create(const pdk_csr* pre, int32_t P, int32_t C, int32_t S,
     all_req.push_back(base + ch_parts[c1] - ch_parts[c0] + suf_parts[b + 1] - suf_parts[b]);
   }
   plan->n_chunks = (int32_t)owner.size();
+  plan->ch_nnz = (int32_t)ch_indices.size();
+  plan->suf_nnz = suf->nnz;
   plan->n_pre_parts = ch_parts.back();
   plan->n_suf_parts = suf_parts.back();
   auto& bl = plan->blob;
@@ -871,14 +876,15 @@ int run_chunked(const pdk_chunked_plan* plan, const pdk_kv_pool* pre_pool,
     float* v_all = (float*)(w + L.v_all);
     float* l_all = (float*)(w + L.l_all);
     if (plan->n_pre_parts > 0) {
-      pdk_csr vc{base + o.ch_indptr, base + o.ch_indices, base + o.ch_len, plan->n_chunks, 0};
+      pdk_csr vc{base + o.ch_indptr, base + o.ch_indices, base + o.ch_len, plan->n_chunks,
+                 plan->ch_nnz};
       st = partial_rows(pre_pool, &vc, q, q_dtype, Hq, sm_scale, plan->S, base + o.ch_parts,
                         plan->n_pre_parts, base + o.ch_slots, base + o.ch_owner, 1, G,
                         base + o.all_row_ch, v_all, l_all, stream, nullptr, T, 0);
       if (st) return st;
     }
     if (plan->n_suf_parts > 0) {
-      pdk_csr vs{base + o.suf_indptr, base + o.suf_indices, base + o.suf_len, B, 0};
+      pdk_csr vs{base + o.suf_indptr, base + o.suf_indices, base + o.suf_len, B, plan->suf_nnz};
       st = partial_rows(suf_pool, &vs, q, q_dtype, Hq, sm_scale, plan->Ss, base + o.suf_parts,
                         plan->n_suf_parts, nullptr, nullptr, 0, G, base + o.all_row_suf, v_all,
                         l_all, stream, nullptr, T, 1);
@@ -889,7 +895,8 @@ int run_chunked(const pdk_chunked_plan* plan, const pdk_kv_pool* pre_pool,
   }
   // chunk partials: each (request, chunk) is a view request with one member
   if (plan->n_pre_parts > 0) {
-    pdk_csr vc{base + o.ch_indptr, base + o.ch_indices, base + o.ch_len, plan->n_chunks, 0};
+    pdk_csr vc{base + o.ch_indptr, base + o.ch_indices, base + o.ch_len, plan->n_chunks,
+                 plan->ch_nnz};
     st = partial_rows(pre_pool, &vc, q, q_dtype, Hq, sm_scale, plan->S, base + o.ch_parts,
                       plan->n_pre_parts, base + o.ch_slots, base + o.ch_owner, 1, G,
                       base + o.ch_parts, (float*)(w + L.v_pre), (float*)(w + L.l_pre), stream,
@@ -906,7 +913,7 @@ int run_chunked(const pdk_chunked_plan* plan, const pdk_kv_pool* pre_pool,
   if (st) return st;
   // suffix partials and their merge -> odd rows
   if (plan->n_suf_parts > 0) {
-    pdk_csr vs{base + o.suf_indptr, base + o.suf_indices, base + o.suf_len, B, 0};
+    pdk_csr vs{base + o.suf_indptr, base + o.suf_indices, base + o.suf_len, B, plan->suf_nnz};
     st = partial_rows(suf_pool, &vs, q, q_dtype, Hq, sm_scale, plan->Ss, base + o.suf_parts,
                       plan->n_suf_parts, nullptr, nullptr, 0, G, base + o.suf_parts,
                       (float*)(w + L.v_suf), (float*)(w + L.l_suf), stream, nullptr, T, 1);

@@ -66,6 +66,30 @@ __device__ __forceinline__ void xcd_unit_tile(int block, int n_rt, int& unit, in
   tile = r >> 3;
 }
 
+// Partition p of view request b: the request's first page-id index page0 and
+// the token range [start, end) the partition covers. The request's page-id
+// offsets are clamped to [0, nnz) and the range to its pages and length, so
+// a malformed device page table (offsets outside the page ids, fewer pages
+// than the length needs, a negative partition) gives wrong numbers or an
+// empty range but never a read outside the page ids; the kernels read an id
+// outside [0, num_blocks) as pool row 0, on every path.
+__host__ __device__ inline void part_range(const PartialArgs& a, int b, int p, int& page0,
+                                           int& start, int& end) {
+  int lo = a.indptr[b], hi = a.indptr[b + 1];
+  lo = lo < 0 ? 0 : (lo > a.nnz ? a.nnz : lo);
+  hi = hi < lo ? lo : (hi > a.nnz ? a.nnz : hi);
+  page0 = lo;
+  const long long cap = INT_MAX / 2;
+  long long s = p > 0 ? (long long)p * a.S : 0;
+  s = s < cap ? s : cap;
+  long long e = s + a.S;
+  const long long n = a.kv_len[b], tokens = (long long)(hi - lo) * a.P;
+  e = e < n ? e : n;
+  e = e < tokens ? e : tokens;
+  start = (int)s;
+  end = (int)(e > s ? e : s);
+}
+
 // Exclusive end of the positions row group n sees (INT_MAX: the whole range).
 __device__ __forceinline__ int visible_end(const PartialArgs& a, int b, int n) {
   if (!a.causal) return INT_MAX;
