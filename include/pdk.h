@@ -177,6 +177,26 @@ int pdk_decode_flat(const pdk_kv_pool* pool, const pdk_csr* csr_dev, const void*
                     int32_t num_partitions, float* out, float* lse_out, void* workspace,
                     size_t workspace_bytes, hipStream_t stream);
 
+/* pdk_decode_flat without a workspace, for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). The partial states live in a static device array
+ * of PDK_DECODE_FLAT_NOALLOC_MAX_BYTES (32 MiB), one per device, held from
+ * the library's first use on that device until the process ends; its
+ * address is looked up once per device on the first call there. Calls that
+ * need more, pdk_decode_flat_workspace_bytes(num_partitions, Hq, head_dim_v)
+ * > the maximum (at Hq 32 and head dim 128: more than 2,032 partitions),
+ * fail with PDK_ERR_WORKSPACE before any launch. Nothing is allocated or
+ * freed. Every call on one device shares that device's array: calls that
+ * overlap on one device (two streams, or two host threads) race and give
+ * wrong results; calls ordered on one stream are safe (each call writes
+ * every state row it reads). Other arguments and errors: pdk_decode_flat. */
+#define PDK_DECODE_FLAT_NOALLOC_MAX_BYTES ((size_t)32 << 20)
+int pdk_decode_flat_noalloc(const pdk_kv_pool* pool, const pdk_csr* csr_dev, const void* q,
+                            int32_t q_dtype, int32_t num_q_heads, float sm_scale,
+                            int32_t partition_tokens, const int32_t* part_indptr_dev,
+                            int32_t num_partitions, float* out, float* lse_out,
+                            hipStream_t stream);
+
 /* Multi-token steps: q_tokens = T >= 1 query tokens per request in one
  * step (verification of speculated tokens, chunked prefill of a few tokens).
  * q [batch, T, Hq, Dk] (f32|bf16); the request's range (kv_len tokens)

@@ -31,6 +31,7 @@ __all__ = [
     "cascade_tuning_clear",
     "partition_indptr", "validate_csr", "parse_switch", "cascade_enabled_from_env",
     "stacked_head_map", "paged_decode_partial", "merge_states", "decode_flat",
+    "decode_flat_noalloc", "DECODE_FLAT_NOALLOC_MAX_BYTES",
     "paged_multi_token_partial", "multi_token_flat",
     "stack_heads", "unstack_heads", "fp8_dequant_bf16",
     "F32", "BF16", "FP8_E4M3", "DECLINE_NAMES",
@@ -86,6 +87,7 @@ _SIGS = {
     "pdk_merge_states": (_I, [_P, _P, _I, _P, _I, _I, _I, _P, _P, _P]),
     "pdk_decode_flat_workspace_bytes": (_S, [_I, _I, _I]),
     "pdk_decode_flat": (_I, [_P, _P, _P, _I, _I, _F, _I, _P, _I, _P, _P, _P, _S, _P]),
+    "pdk_decode_flat_noalloc": (_I, [_P, _P, _P, _I, _I, _F, _I, _P, _I, _P, _P, _P]),
     "pdk_stack_heads": (_I, [_P, _I, _P, _I, _I, _I, _I, _P, _P]),
     "pdk_unstack_heads": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P]),
     "pdk_fp8_dequant_bf16": (_I, [_P, _L, _F, _P, _P]),
@@ -351,6 +353,25 @@ def decode_flat(pool: KVPool, csr: DeviceCSR, q: torch.Tensor, sm_scale: float,
                                  Hq, float(sm_scale), int(partition_tokens), _ptr(part_indptr),
                                  int(num_partitions), _ptr(out), _ptr(lse_out), _ptr(workspace),
                                  int(workspace.numel()), _stream(stream)))
+    return out, lse_out
+
+
+DECODE_FLAT_NOALLOC_MAX_BYTES = 32 << 20
+
+
+def decode_flat_noalloc(pool: KVPool, csr: DeviceCSR, q: torch.Tensor, sm_scale: float,
+                        partition_tokens: int, part_indptr: torch.Tensor, num_partitions: int,
+                        out: torch.Tensor, lse_out: Optional[torch.Tensor] = None, stream=None):
+    """decode_flat with the partial states in the library's static device
+    array (no workspace): out [B, Hq, Dv] and lse_out [B, Hq] are the
+    caller's. Calls that overlap on one device race."""
+    Hq = int(q.shape[1])
+    ps, cs = pool.struct(), csr.struct()
+    _check(lib().pdk_decode_flat_noalloc(ctypes.byref(ps), ctypes.byref(cs), _ptr(q),
+                                         _dtype_code(q), Hq, float(sm_scale),
+                                         int(partition_tokens), _ptr(part_indptr),
+                                         int(num_partitions), _ptr(out), _ptr(lse_out),
+                                         _stream(stream)))
     return out, lse_out
 
 
