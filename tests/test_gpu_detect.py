@@ -1,17 +1,21 @@
-"""Shared-prefix detection on the device (page ids only on the GPU) against
-the host planner [cascade-PR, "Detection reads the page table, not the
-refcounts"]: every plan field, the stats and the decline reason equal the
-host plan's for the same table, nested spans included; the views' page ids,
-gathered on the device at upload, give bit-identical decode outputs; tables
-with thousands of requests (the grouping scan crosses many 64-request
-chunks) and every rejection case; misuse is refused."""
+"""Shared-prefix detection on the device (page ids only on the GPU)
+[cascade-PR, "Detection reads the page table, not the refcounts"]: every
+plan field, the stats and the decline reason equal the oracle planner's
+(oracle/planner.py, and oracle/nested.py for nested spans) and the host
+planner's for the same table; decode outputs of the device plan (its views'
+page ids gathered on the device at upload) are bit-identical to the host
+plan's and within the bf16 bar of the oracle's attention;
+tables with thousands of requests (the grouping scan crosses many
+64-request chunks) and every rejection case; misuse is refused."""
 import numpy as np
 import pytest
 import torch
 
 import paged_split_kv_v2_amd as pdk
 import workloads as W
-from gpu_util import to_device
+from gpu_util import TOL, assert_close, assert_lse, to_device
+from oracle import attention as oatt
+from plan_expect import expected_plan
 
 pytestmark = pytest.mark.gpu
 
@@ -20,12 +24,22 @@ FIELDS = ("members", "group_indptr", "span_pages", "span_start", "span_parent", 
           "member_rank")
 
 
-def both(gpu, indptr, indices, kv_len, P, params):
+def both(gpu, indptr, indices, kv_len, P, **kw):
+    """The device-detected plan against the oracle's plan and the host
+    plan, field by field; returns (host plan, device plan)."""
+    params = gpu.CascadeParams(**kw)
     host = gpu.CascadePlan(indptr, indices, kv_len, P, params)
     csr = gpu.DeviceCSR.from_host(indptr, indices, kv_len)
     dev = gpu.CascadePlan.from_device(csr, indptr, kv_len, P, params)
+    want, stats, decline = expected_plan(indptr, indices, kv_len, P, kw)
     for f in FIELDS:
+        assert np.array_equal(dev.field(f).astype(np.int64),
+                              np.asarray(want[f], np.int64)), f
         assert np.array_equal(host.field(f), dev.field(f)), f
+    got_stats, got_decline = dev.stats()
+    assert got_decline == decline
+    if stats is not None:
+        assert got_stats == stats
     assert host.stats() == dev.stats()
     assert dev.field("l0_indices").size == 0 and dev.field("l1_indices").size == 0
     return host, dev
@@ -59,16 +73,14 @@ def test_device_plan_equals_host_plan_on_random_tables(gpu, max_groups):
     for B, groups in ((7, 2), (130, 5), (3000, 40)):
         ip, ix, kl = random_shared_table(rng, B, groups)
         for mp, mm in ((1, 2), (4, 3), (2, 20)):
-            params = gpu.CascadeParams(enabled=1, max_groups=max_groups, min_shared_pages=mp,
-                                       min_members=mm, l0_partition_tokens=64,
-                                       l1_partition_tokens=128)
-            both(gpu, ip, ix, kl, 16, params)
+            both(gpu, ip, ix, kl, 16, enabled=1, max_groups=max_groups, min_shared_pages=mp,
+                 min_members=mm, l0_partition_tokens=64, l1_partition_tokens=128)
 
 
 def test_declines_match(gpu):
     b = W.llama3_8b_flat(seed=2610, batch=9, min_len=10, max_len=900, poison=False)
     for enabled in (0, 1):
-        _, dev = both(gpu, b.indptr, b.indices, b.kv_len, 16, gpu.CascadeParams(enabled=enabled))
+        _, dev = both(gpu, b.indptr, b.indices, b.kv_len, 16, enabled=enabled)
         assert dev.stats()[1] == ("disabled" if enabled == 0 else "no_candidate")
 
 
@@ -76,13 +88,15 @@ def test_device_plan_runs_bit_identical(gpu):
     b = W.cascade_shared_prefix(seed=2620, groups=3, members=6, prefix_tokens=1024,
                                 suffix_max=300, extra=3, extra_tokens=700)
     pool, csr, q = to_device(b)
-    params = gpu.CascadeParams(enabled=1, max_groups=0, l0_partition_tokens=256,
-                               l1_partition_tokens=512)
-    host, dev = both(gpu, b.indptr, b.indices, b.kv_len, b.page_size, params)
+    host, dev = both(gpu, b.indptr, b.indices, b.kv_len, b.page_size, enabled=1, max_groups=0,
+                     l0_partition_tokens=256, l1_partition_tokens=512)
     ho, hl = host.run(pool, q, b.sm_scale)
     do, dl = dev.run(pool, q, b.sm_scale)
     torch.cuda.synchronize()
     assert torch.equal(ho, do) and torch.equal(hl, dl)
+    ro, rl = oatt.decode_attention(b)
+    assert_close(do.cpu().numpy(), ro, TOL["bf16"], "device-planned cascade out")
+    assert_lse(dl.cpu().numpy(), rl, "device-planned cascade lse")
 
 
 def test_misuse_is_refused(gpu):
@@ -137,10 +151,9 @@ def test_device_nested_plans_equal_host_plans(gpu, max_depth):
     for B in (6, 40, 300):
         for _ in range(6):
             ip, ix, kl = random_nested_table(rng, B)
-            params = gpu.CascadeParams(enabled=1, max_groups=0, min_shared_pages=1,
-                                       max_depth=max_depth, l0_partition_tokens=64,
-                                       l1_partition_tokens=128)
-            host, _ = both(gpu, ip, ix, kl, 16, params)
+            host, _ = both(gpu, ip, ix, kl, 16, enabled=1, max_groups=0, min_shared_pages=1,
+                           max_depth=max_depth, l0_partition_tokens=64,
+                           l1_partition_tokens=128)
             deep += int((host.field("span_parent") >= 0).sum())
     assert deep > 0    # the tables do produce nested spans
 
@@ -150,9 +163,8 @@ def test_device_nested_plan_runs_bit_identical(gpu):
                                tenant_tokens=256, suffix_min=1, suffix_max=200, extra=2,
                                extra_tokens=300)
     pool, csr, q = to_device(b)
-    params = gpu.CascadeParams(enabled=1, max_groups=0, max_depth=2, l0_partition_tokens=256,
-                               l1_partition_tokens=256)
-    host, dev = both(gpu, b.indptr, b.indices, b.kv_len, b.page_size, params)
+    host, dev = both(gpu, b.indptr, b.indices, b.kv_len, b.page_size, enabled=1, max_groups=0,
+                     max_depth=2, l0_partition_tokens=256, l1_partition_tokens=256)
     assert len(host.field("span_pages")) == 4     # system prompt + 3 tenant spans
     ho, hl = host.run(pool, q, b.sm_scale)
     do, dl = dev.run(pool, q, b.sm_scale)

@@ -6,25 +6,11 @@ import pytest
 
 import paged_split_kv_v2_amd as pdk
 from oracle import planner as oplan
+from plan_expect import fused_rows, nested_expected
 from workloads import cascade_shared_prefix, tiny_gqa_fp32
 
 FIELDS = ["members", "group_indptr", "span_pages", "l0_indptr", "l0_indices", "l0_len",
           "l1_indptr", "l1_indices", "l1_len", "merge_indptr", "group_of", "member_rank"]
-
-
-def fused_rows(group_of, l0_len, l1_len, params):
-    """The library's single-merge row layout, written out from its reading
-    (not a rule of the page, which pairs one level-0 and one level-1 state
-    per member): request b owns ceil(l0_len/S0) rows for the span holding it
-    (none for a non-member), then max(1, ceil(l1_len/S1)) level-1 rows, so an
-    empty level-1 range still owns the (0, -inf) row its merge reads."""
-    S0, S1 = int(params.l0_partition_tokens), int(params.l1_partition_tokens)
-    out = [0]
-    for b in range(len(l1_len)):
-        k = int(group_of[b])
-        n0 = -(-int(l0_len[k]) // S0) if k >= 0 else 0
-        out.append(out[-1] + n0 + max(1, -(-int(l1_len[b]) // S1)))
-    return np.asarray(out, dtype=np.int32)
 
 
 def test_fused_rows_with_an_empty_level1_range():
@@ -122,39 +108,6 @@ def test_invalid_plan_arguments():
     with pytest.raises(pdk.PdkError):
         pdk.CascadePlan([0, 1], [3], [16], 16,
                         pdk.CascadeParams(enabled=1, l1_partition_tokens=24))
-
-
-def nested_expected(indptr, indices, kv_len, P, params, depth):
-    """The arrays the library's plan must hold, from the oracle's nested plan."""
-    from oracle import nested
-    ref = nested.build_nested_plan(indptr, indices, kv_len, P, params, depth)
-    B = len(kv_len)
-    members, gptr, l0_idx, l0_ptr = [], [0], [], [0]
-    for sp in ref.spans:
-        members += sp.members
-        gptr.append(len(members))
-        b0 = sp.members[0]
-        l0_idx += list(indices[indptr[b0] + sp.start_page:indptr[b0] + sp.start_page + sp.span_pages])
-        l0_ptr.append(len(l0_idx))
-    group_of, rank = [-1] * B, [-1] * B
-    for k, sp in enumerate(ref.spans):
-        if sp.depth == 0:
-            for m, b in enumerate(sp.members):
-                group_of[b], rank[b] = k, m
-    l1_idx, l1_ptr, l1_len = [], [0], []
-    for b in range(B):
-        s = int(ref.private_start_page[b])
-        l1_idx += list(indices[indptr[b] + s:indptr[b + 1]])
-        l1_ptr.append(len(l1_idx))
-        l1_len.append(int(kv_len[b]) - s * P)
-    return ref, {"members": members, "group_indptr": gptr,
-                 "span_pages": [s.span_pages for s in ref.spans],
-                 "span_start": [s.start_page for s in ref.spans],
-                 "span_parent": [s.parent for s in ref.spans],
-                 "l0_indptr": l0_ptr, "l0_indices": l0_idx,
-                 "l0_len": [s.span_pages * P for s in ref.spans],
-                 "l1_indptr": l1_ptr, "l1_indices": l1_idx, "l1_len": l1_len,
-                 "merge_indptr": ref.merge_indptr, "group_of": group_of, "member_rank": rank}
 
 
 @pytest.mark.parametrize("depth", [2, 3])
