@@ -446,6 +446,432 @@ void partial_latent_kernel(const PartialArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// fp8 latent pools: 4 waves (one per SIMD), 32 query rows per wave.
+//
+// Every K or V^T fragment read from LDS feeds a 32-row product
+// (v_mfma_f32_32x32x16_bf16): half the LDS bytes per flop of 16-row
+// fragments. With 128 rows and 576-wide rows the products are bound by LDS
+// read bandwidth (128 B per clock per CU) rather than by the matrix cores.
+// Each wave keeps Q^T for its 32 rows (36 B fragments, 144 registers) and
+// O^T = 512 dims x 32 rows (16 blocks of 32 x 32, the 256 accumulator
+// registers) for the whole partition: one wave per SIMD has the 512
+// registers for both.
+//   * S^T = K . Q^T per 32-token tile: A = K (32 tokens x 16 dims, one
+//     16-byte LDS read per lane), B = Q^T (16 dims x 32 rows); lane j holds
+//     S^T[token 8(r/4) + 4(j/32) + r%4][row j%32] in register r.
+//   * O^T += V^T . P^T in two 16-token k-steps: B = P^T straight from the S^T
+//     registers (k slot i of lane j = register 8kk + i, i.e. tokens
+//     16kk + 4(j/32) + {0..3}, then 16kk + 8 + 4(j/32) + {0..3}); A = V^T
+//     (32 dims x those 16 tokens) from the row-major tile by two transposing
+//     loads (ds_read_b64_tr_b16: in each group of 16 lanes, lane i receives
+//     element i%4 of the 8 bytes addressed by lane 4e + i/4 as its element
+//     e; lane 16g + 4e + s addresses token 4(g/2) + e, dims 16(g%2) + 4s).
+//   * Tiles are stored bf16 [token][576] with 16-byte chunk c of token t at
+//     position c ^ f(t) within its aligned group of 8 chunks, f(t) bits:
+//     b0 = t2, b1 = t0 ^ t3, b2 = t1. Rows are 1152 bytes apart, so with
+//     LDS banks 128 or 256 bytes wide alike, the K reads (8 or 16
+//     consecutive tokens, one chunk), the transposing reads (4 tokens x 2
+//     or x 4 chunks per bank cycle) and the dequantized stores are free of
+//     bank conflicts (f was chosen by checking every access pattern under
+//     both bank widths).
+// Fetch: the fp8 rows of tile i + 2 go through registers during interval
+// i, lane L taking token L/8 and 8-code units (L%8) + 8k, k < 9 (each fetch
+// instruction reads 64 contiguous bytes per token, each LDS store fills one
+// 128-byte bank line per token); each lane dequantizes its own units
+// (RNE_bf16(f32(x) * scale)) into a bf16 LDS buffer one interval later. No
+// global->LDS loads, so no LDS access waits for a fetch.
+// Interval i (one barrier; three buffers): the S^T chain of tile i (36
+// dependent products) interleaved with O^T of tile i - 1 (32 products on 16
+// independent accumulators, k-step major), so that the matrix core always
+// has an independent product to start; the dequantization of tile i + 1
+// and the fetch of tile i + 2 spread over the same loop; then the softmax
+// of tile i. The S^T products are written as inline asm with VGPR operands
+// and the O^T products with accumulation-register operands: the compiler
+// otherwise gives every product's accumulator the same register file and
+// has no room for both.
+// Measured (32 requests x 16384 fp8 tokens, 2048-token partitions): 165 us
+// per launch against 195 us for the 8-wave kernel above; with the matrix
+// cores 38% busy by counter, LDS 24% busy, no bank conflicts. Timing
+// variants put the products alone at about 62% of the matrix-core rate
+// and show the dequantization and the softmax not hidden behind them: with
+// one wave per SIMD no other wave fills the issue slots they take.
+// Softmax reference: a row's scores are exponentiated against a fixed
+// reference, its maximum over the first tile it sees, and the accumulators
+// are never rescaled (a VALU rescale of accumulator registers costs the
+// registers the products need). A later score more than kRefL (log2 units)
+// above the reference would overflow that scheme: then the whole workgroup
+// restarts the partition with the raised reference, accumulators zeroed. The
+// result is the same exact softmax either way; the restart costs a second
+// pass and happens only for scores that grow by more than 2^kRefL within a
+// partition.
+// ---------------------------------------------------------------------------
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+constexpr float kRefL = 16.f;
+
+// chunk swizzle of token t (see above)
+__device__ __forceinline__ int fswz(int t) {
+  return ((t >> 2) & 1) | (((t ^ (t >> 3)) & 1) << 1) | (((t >> 1) & 1) << 2);
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void partial_latent_fp8_kernel(const PartialArgs a) {
+  constexpr int NW = 4;                   // waves, one per SIMD
+  constexpr int RW = 32;                  // query rows per wave
+  constexpr int ROWS = NW * RW;           // 128
+  constexpr int NT = 64 * NW;
+  constexpr int KS = DK / 16;             // k-steps of S^T (16 dims)
+  constexpr int DB = DV / 32;             // 32-dim output blocks
+  constexpr int RB = DK * 2;              // bytes of a bf16 tile row
+  constexpr int CPR = DK / 8;             // 16-byte bf16 chunks (8-code units) per row
+  constexpr int UPL = CPR / 8;            // units per lane and tile
+  static_assert(CPR % 8 == 0 && NT == 8 * kTT, "8 lanes per token, whole units per lane");
+  static_assert(RB % 128 == 0 && DK % 64 == 0 && DV % 64 == 0 && DV <= DK, "latent shapes");
+
+  // three bf16 tile buffers, chosen at run time (no global->LDS loads, so
+  // nothing needs the compiler to tell them apart)
+  __shared__ __align__(16) uint16_t sbuf[3][kTT * DK];
+  __shared__ int sm_pid[kMaxPagesL];
+  __shared__ int sm_restart;
+
+  const int n_tiles = (a.max_rows + ROWS - 1) / ROWS;
+  int unit, tile;
+  xcd_unit_tile(blockIdx.x, n_tiles, unit, tile);
+  if (unit >= a.num_parts * a.Hkv) return;  // grid padding (uniform)
+  const int h = unit % a.Hkv;
+  const int r = unit / a.Hkv;
+  const int tid = threadIdx.x;
+
+  int b = 0, p;
+  if (a.work != nullptr) {
+    const int2 it = a.work[r];
+    b = it.x;
+    p = it.y;
+  } else {
+    for (int base = 1; base < a.batch; base += 64) {
+      const int i = base + (tid & 63);
+      const bool le = (i < a.batch) && (a.part_indptr[i] <= r);
+      b += __popcll(__ballot(le));
+    }
+    p = r - a.part_indptr[b];
+  }
+  const bool stacked = a.member_indptr != nullptr;
+  const int mbase = stacked ? a.member_indptr[b] : 0;
+  const int nrows = view_rows(a, stacked, mbase, b);
+  const int row0 = tile * ROWS;
+  if (row0 >= nrows) return;  // uniform
+
+  int page0, start, end;
+  part_range(a, b, p, page0, start, end);
+  // causal rows: the tile loop stops at the last owned row's end; every
+  // owned row sees at least the positions below end_lo (uniform)
+  const int end_lo = min(end, visible_end(a, b, row0 / a.G));
+  end = min(end, visible_end(a, b, (min(row0 + ROWS, nrows) - 1) / a.G));
+  const int shift = a.p_shift;
+  const int pmask = a.P - 1;
+  const int pg_first = start >> shift;
+  if (end > start) {
+    const int n_pg = ((end - 1) >> shift) - pg_first + 1;
+    for (int i = tid; i < n_pg; i += NT) {
+      const int pid = a.indices[page0 + pg_first + i];
+      // an id outside the pool reads row 0 (see part_range)
+      sm_pid[i] = ((unsigned)pid < (unsigned)a.num_blocks) ? pid : 0;
+    }
+  }
+  if (tid == 0) sm_restart = 0;
+
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int hf = lane >> 5;    // lane half
+  const int n32 = lane & 31;   // query row of the wave (MFMA column) / token of a K read
+  const int my_row = row0 + RW * wave + n32;
+  const bool live_wave = row0 + RW * wave < nrows;  // uniform over the wave
+  const int my_end = min(end, visible_end(a, b, min(my_row, nrows - 1) / a.G));
+
+  // Q^T fragments: lane -> row n32, dims 16ks + 8hf + 0..7
+  u32x4_t qf[KS];
+  {
+    int qb = b, head = 0;
+    const bool live = my_row < nrows;
+    if (live) {
+      const int m = my_row / a.G, g = my_row % a.G;
+      qb = query_row(a, stacked, mbase, b, m);
+      head = h * a.G + g;
+    }
+    // row 0 of request qb stands in for padding rows: always a valid address
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
+                         ((size_t)qb * a.Hq + head) * DK + 8 * hf;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(qp + 16 * ks);
+      qf[ks] = live ? x : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  }
+
+  const char* kbase = reinterpret_cast<const char*>(a.k) + (size_t)h * a.k_hstride;
+  const long long kb_stride = a.k_bstride;
+
+  // Unit k of lane tid: token tt = tid / 8, 8 codes at dims 8c, c = tid % 8
+  // + 8k, stored at chunk position 8k + ((tid % 8) ^ f(tt)); a tile never
+  // crosses a page (P is a multiple of the tile); rows past the end repeat
+  // the last token.
+  const int u_tt = tid >> 3;
+  const int u_lds = u_tt * RB + 16 * ((tid & 7) ^ fswz(u_tt));  // + 128 k
+  auto fetch = [&](int t0, u32x2_t (&F)[UPL]) {
+    const int pid = __builtin_amdgcn_readfirstlane(sm_pid[(t0 >> shift) - pg_first]);
+    const char* pbase = kbase + pid * kb_stride + (long long)(t0 & pmask) * DK;
+    const char* src = pbase + min(u_tt, end - 1 - t0) * DK + 8 * (tid & 7);  // + 64 k
+#pragma unroll
+    for (int k = 0; k < UPL; ++k) F[k] = *reinterpret_cast<const u32x2_t*>(src + 64 * k);
+  };
+  auto convert = [&](const u32x2_t (&F)[UPL], uint16_t* dst) {
+    char* d = reinterpret_cast<char*>(dst) + u_lds;
+#pragma unroll
+    for (int k = 0; k < UPL; ++k) {
+      uint32_t w[4];
+      fp8x4_dequant_bf16(F[k][0], a.k_scale, w[0], w[1]);
+      fp8x4_dequant_bf16(F[k][1], a.k_scale, w[2], w[3]);
+      *reinterpret_cast<u32x4_t*>(d + 128 * k) = u32x4_t{w[0], w[1], w[2], w[3]};
+    }
+  };
+
+  // Per-lane LDS byte offsets (chunk bits XOR-swizzled by token):
+  //   K read of k-step ks: token n32, chunk 2ks + hf -> position
+  //     8(ks/4) + (2(ks%4) ^ z), z = hf ^ f(n32):
+  //     kofs ^ 32(ks%4) + 128(ks/4), kofs = n32*RB + 16z;
+  //   V^T reads of block db, k-step kk: token 16kk + T0 (+ 8), chunk
+  //     4db + c, c = 2(g%2) + s/2 -> position 8(db/2) + (4(db%2) ^ x),
+  //     x = c ^ f(T0) (f(T0 + 8) = f(T0) ^ 2, f(T + 16) = f(T)):
+  //     vofs ^ 64(db%2) (^ 32) + 128(db/2) + (16kk (+8)) RB,
+  //     vofs = T0*RB + 16x + 8(s%2), T0 = 4(g/2) + e.
+  const int kofs = n32 * RB + 16 * (hf ^ fswz(n32));
+  int vofs;
+  {
+    const int g = lane >> 4, e = (lane >> 2) & 3, s = lane & 3;
+    const int T0 = 4 * (g >> 1) + e;
+    const int x = (2 * (g & 1) + (s >> 1)) ^ fswz(T0);
+    vofs = T0 * RB + 16 * x + 8 * (s & 1);
+  }
+
+  f32x16_t acc[DB];
+  float ref = -INFINITY, run_l = 0.f;  // per row (both lane halves agree)
+
+  // One step of the S^T chain, written out so that the accumulator stays in
+  // ordinary VGPRs while the O^T accumulators fill the 256 accumulation
+  // registers (the compiler otherwise puts every product's accumulator in
+  // the accumulation file and has no room for both). gfx950 interlocks a
+  // product on its predecessor's result (the chain needs no wait states),
+  // the first step starts from the inline constant 0 (no VALU write of the
+  // accumulator is ever read), and after the last step the 12 wait states
+  // an XDL result needs before a VALU reads it are inserted here, since the
+  // compiler does not see this product.
+  auto qk_step = [&](int st, const u32x4_t& kfr, const u32x4_t& qfr, f32x16_t& s) {
+    if (st == 0) {
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(s) : "v"(kfr), "v"(qfr));
+    } else if (st < KS - 1) {
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(kfr), "v"(qfr));
+    } else {
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 4"
+                   : "+v"(s) : "v"(kfr), "v"(qfr));
+    }
+  };
+
+  // One O^T product, written out so that its accumulator stays in the
+  // accumulation registers. The accumulators are written only by these
+  // products (zeroed once per pass, followed by the wait states a product
+  // reading them needs) and read only after the tile loop (after the wait
+  // states an XDL result needs). P^T comes from VALU instructions: the first
+  // product of an interval waits the 2 states an XDL source written by VALU
+  // needs.
+  auto pv_step = [&](int st, const u32x4_t& vfr, const bf16x8_t& pbr, f32x16_t& o) {
+    if (st == 0) {
+      asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                   : "+a"(o) : "v"(vfr), "v"(pbr));
+    } else {
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(vfr), "v"(pbr));
+    }
+  };
+
+  // One interval's products: S^T of tile `cur` (a chain of KS dependent
+  // MFMAs) interleaved with O^T += V^T . P^T of the tile before it (2 DB
+  // MFMAs on DB independent accumulators, k-step major), so that the matrix
+  // core always has an independent product to start while the S^T chain
+  // waits for its previous step; the dequantization of the next tile and
+  // the fetch of the one after it are spread over the same loop, one unit
+  // every few steps. K fragments are read KP steps ahead, V^T fragments VP
+  // steps ahead, into rings of registers (deeper rings measured no faster).
+  // The dequantization and fetch always run (past the last tile they repeat
+  // it: same bytes, unused buffer).
+  auto products = [&](const uint16_t* cur, const uint16_t* prev, const bf16x8_t (&pb)[2],
+                      f32x16_t& s, uint16_t* next, u32x2_t (&F)[UPL], int t_fetch) {
+    constexpr int KP = 2, VP = 2, NPV = 2 * DB;
+    constexpr int STEPS = KS > NPV ? KS : NPV;
+    constexpr int CONV_EVERY = STEPS / UPL;
+    static_assert(CONV_EVERY >= 1, "unit spacing");
+    const char* tk = reinterpret_cast<const char*>(cur);
+    const char* tv = reinterpret_cast<const char*>(prev);
+    int k0, v0;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(k0) : "v"(kofs));
+    asm volatile("v_mov_b32 %0, %1" : "=v"(v0) : "v"(vofs));
+    auto kread = [&](int ks) {
+      return *reinterpret_cast<const u32x4_t*>(tk + (k0 ^ (32 * (ks & 3))) + 128 * (ks >> 2));
+    };
+    auto vread = [&](int i) {  // i = DB kk + db
+      const int kk = i / DB, db = i % DB;
+      const char* p0 = tv + (v0 ^ (64 * (db & 1))) + 128 * (db >> 1) + 16 * kk * RB;
+      const char* p1 = tv + (v0 ^ (64 * (db & 1) + 32)) + 128 * (db >> 1) + (16 * kk + 8) * RB;
+      const u32x2_t x0 = __builtin_bit_cast(
+          u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p0));
+      const u32x2_t x1 = __builtin_bit_cast(
+          u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p1));
+      return u32x4_t{x0[0], x0[1], x1[0], x1[1]};
+    };
+    // the tile after next (page uniform over the tile)
+    const int pid = __builtin_amdgcn_readfirstlane(sm_pid[(t_fetch >> shift) - pg_first]);
+    const char* src = kbase + pid * kb_stride + (long long)(t_fetch & pmask) * DK +
+                      min(u_tt, end - 1 - t_fetch) * DK + 8 * (tid & 7);
+    char* dst = reinterpret_cast<char*>(next) + u_lds;
+    u32x4_t kf[KP + 1], vf[VP + 1];
+#pragma unroll
+    for (int i = 0; i < KP; ++i) kf[i] = kread(i);
+#pragma unroll
+    for (int i = 0; i < VP; ++i) vf[i] = vread(i);
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+      if (st < KS) {
+        if (st + KP < KS) kf[(st + KP) % (KP + 1)] = kread(st + KP);
+        qk_step(st, kf[st % (KP + 1)], qf[st], s);
+      }
+      if (st < NPV) {
+        if (st + VP < NPV) vf[(st + VP) % (VP + 1)] = vread(st + VP);
+        pv_step(st, vf[st % (VP + 1)], pb[st / DB], acc[st % DB]);
+      }
+      if (st % CONV_EVERY == CONV_EVERY - 1 && st / CONV_EVERY < UPL) {
+        const int k = st / CONV_EVERY;
+        uint32_t w[4];
+        fp8x4_dequant_bf16(F[k][0], a.k_scale, w[0], w[1]);
+        fp8x4_dequant_bf16(F[k][1], a.k_scale, w[2], w[3]);
+        *reinterpret_cast<u32x4_t*>(dst + 128 * k) = u32x4_t{w[0], w[1], w[2], w[3]};
+        F[k] = *reinterpret_cast<const u32x2_t*>(src + 64 * k);
+      }
+    }
+  };
+
+  // online softmax of one tile's scores against the row's reference; a
+  // score far above it asks for a restart with the reference raised.
+  // Returns P^T for the two k-steps of the PV product.
+  auto softmax = [&](f32x16_t& s, int t0, int pass, bf16x8_t (&pb)[2]) {
+    float cs = a.scale_log2, mx;
+    if (t0 + kTT <= end_lo) {
+      float hi = s[0], lo = s[0];
+#pragma unroll
+      for (int j = 1; j < 16; ++j) {
+        hi = fmaxf(hi, s[j]);
+        lo = fminf(lo, s[j]);
+      }
+      mx = (cs >= 0.f ? hi : lo) * cs;
+    } else {
+      mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int t = t0 + 8 * (j >> 2) + 4 * hf + (j & 3);
+        s[j] = (t < my_end) ? s[j] * cs : -INFINITY;
+        mx = fmaxf(mx, s[j]);
+      }
+      cs = 1.f;
+    }
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(f32_bits(mx), f32_bits(mx), false, false);
+      mx = fmaxf(bits_f32(sw[0]), bits_f32(sw[1]));  // over lanes l and l ^ 32
+    }
+    if (ref == -INFINITY) ref = mx;  // the first visible tile sets the reference
+    if (__builtin_expect(__any(mx > ref + kRefL), 0)) {
+      ref = fmaxf(ref, mx);
+      sm_restart = pass + 1;
+    }
+    const float mu = (ref == -INFINITY) ? 0.f : ref;
+    uint32_t pw[8];
+#pragma unroll
+    for (int j = 0; j < 16; j += 2) {
+      const float p0 = fast_exp2(__builtin_fmaf(s[j], cs, -mu));
+      const float p1 = fast_exp2(__builtin_fmaf(s[j + 1], cs, -mu));
+      run_l += p0 + p1;
+      pw[j >> 1] = pack_bf16x2_rne(p0, p1);
+    }
+    pb[0] = as_bf16x8(u32x4_t{pw[0], pw[1], pw[2], pw[3]});
+    pb[1] = as_bf16x8(u32x4_t{pw[4], pw[5], pw[6], pw[7]});
+  };
+
+  const int n_tt = (end > start) ? (end - start + kTT - 1) / kTT : 0;
+  const int t_last = start + max(n_tt - 1, 0) * kTT;  // first token of the last tile
+  __syncthreads();  // page ids and the restart flag visible
+  for (int pass = 0;; ++pass) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      acc[db] = f32x16_t{};
+      asm volatile("" : "+a"(acc[db]));  // zeroed in the accumulation registers
+    }
+    asm volatile("s_nop 4" ::: "memory");  // VALU writes before a product reads them
+    run_l = 0.f;
+    u32x2_t F[UPL];
+    if (n_tt > 0) {
+      fetch(start, F);
+      convert(F, sbuf[0]);
+      fetch(min(start + kTT, t_last), F);
+    }
+    lds_barrier();
+    bool restart = false;
+    bf16x8_t pb[2] = {};
+    // interval i: tile i + 1 dequantized into buffer (i + 1) % 3 (and tile
+    // i + 2 fetched), S^T of tile i from buffer i % 3 with O^T of tile
+    // i - 1 from buffer (i + 2) % 3, then the softmax of tile i
+    // Every interval runs the same products (one code path keeps the
+    // registers the allocator needs to the products'): before the first
+    // tile the O^T product reads tile 0 with P = 0 (it adds exact zeros);
+    // past the last tile the S^T product reruns the last tile and its
+    // scores are dropped. Waves whose rows are all padding compute with
+    // zero queries and write nothing.
+    for (int i = 0, bi = 0; i <= n_tt && !restart; ++i, bi = (bi == 2) ? 0 : bi + 1) {
+      const int bp = bi == 0 ? 2 : bi - 1;
+      const uint16_t* cur = sbuf[i < n_tt ? bi : bp];
+      const uint16_t* prev = sbuf[i > 0 ? bp : bi];
+      uint16_t* next = sbuf[bi == 2 ? 0 : bi + 1];
+      const int t_fetch = min(start + (i + 2) * kTT, t_last);
+      f32x16_t s;
+      products(cur, prev, pb, s, next, F, t_fetch);
+      if (live_wave && i < n_tt) softmax(s, start + i * kTT, pass, pb);
+      lds_barrier();  // tiles i - 1 and i read by all waves; tile i + 1 staged
+      restart = sm_restart > pass;  // uniform over the workgroup
+    }
+    if (!restart) break;
+  }
+  // the last products' results before any VALU reads them
+  asm volatile("s_nop 7\n\ts_nop 4" ::: "memory");
+
+  // row sum over the two lane halves, normalized partial and its LSE
+  float l = run_l;
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(f32_bits(l), f32_bits(l), false, false);
+    l = bits_f32(sw[0]) + bits_f32(sw[1]);
+  }
+  if (my_row < nrows) {
+    const int m = my_row / a.G, g = my_row % a.G;
+    const size_t o = state_index(a, stacked, mbase, b, p, m, h * a.G + g);
+    float* dst = a.v_out + o * DV + 4 * hf;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4*>(dst + 32 * db + 8 * q) =
+            make_float4(acc[db][4 * q] * inv, acc[db][4 * q + 1] * inv, acc[db][4 * q + 2] * inv,
+                        acc[db][4 * q + 3] * inv);
+    if (hf == 0) a.lse_out[o] = (l > 0.f) ? ref + log2f(l) : -INFINITY;
+  }
+}
+
 typedef void (*LatentFn)(const PartialArgs);
 
 }  // namespace
@@ -459,20 +885,21 @@ int launch_partial_latent(const PartialArgs& a, hipStream_t stream, bool* handle
   if (a.q_dtype != PDK_BF16 || a.v != nullptr || a.Dk != 576 || a.Dv != 512 ||
       a.max_rows < 64 || a.p_shift < 0 || a.P % kTT != 0)
     return PDK_OK;
-  LatentFn fn = a.kv_dtype == PDK_FP8_E4M3 ? partial_latent_kernel<576, 512, LK_FP8>
-              : a.kv_dtype == PDK_BF16     ? partial_latent_kernel<576, 512, LK_BF16>
-                                           : nullptr;
+  const bool fp8 = a.kv_dtype == PDK_FP8_E4M3;
+  LatentFn fn = fp8 ? partial_latent_fp8_kernel<576, 512>
+              : a.kv_dtype == PDK_BF16 ? partial_latent_kernel<576, 512, LK_BF16>
+                                       : nullptr;
   if (!fn) return PDK_OK;
   if (a.S / a.P + 1 > kMaxPagesL)
     return fail(PDK_ERR_UNSUPPORTED, "partition of %d tokens spans more than %d pages", a.S,
                 kMaxPagesL - 1);
   *handled = true;
-  const int n_tiles = (a.max_rows + kRows - 1) / kRows;
+  const int n_tiles = (a.max_rows + kRows - 1) / kRows;  // both kernels: 128 rows per workgroup
   const long long units = (long long)a.num_parts * a.Hkv;
   const long long blocks = xcd_grid_blocks(units, n_tiles);
   if (blocks == 0) return PDK_OK;
   if (blocks > 0x7FFFFFFFLL) return fail(PDK_ERR_SHAPE, "grid too large (%lld)", blocks);
-  hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(64 * kWaves), 0, stream, a);
+  hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(fp8 ? 256 : 64 * kWaves), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(PDK_ERR_HIP, "latent partial launch: %s", hipGetErrorString(err));
   return PDK_OK;

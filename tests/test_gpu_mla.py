@@ -108,9 +108,9 @@ def test_mla_ragged_and_empty_suffix(gpu):
 
 def test_mla_partitions_of_every_tile_count_mod_three(gpu):
     """Partitions of 3, 5, 6 and 9 tiles of 32 tokens (and a suffix of 3, 4, 2
-    and 1 tiles): the latent kernel cycles three tile buffers, and half of its
-    waves apply a tile's PV product one tile late, so the last tile of a
-    partition sits in each of the three buffers across these cases."""
+    and 1 tiles): the bf16 latent kernel cycles three tile buffers and the
+    fp8 one two, so the last tile of a partition sits in every buffer across
+    these cases."""
     pre_lens, suf_lens = [96, 150, 190, 288], [96, 0, 190, 32]
     pre = W.random_batch(3111, batch=4, page_size=64, num_q_heads=128, num_kv_heads=1,
                          head_dim=576, head_dim_v=512, kv_dtype="fp8_e4m3", q_dtype="bf16",
@@ -127,3 +127,34 @@ def test_mla_partitions_of_every_tile_count_mod_three(gpu):
     assert_lse(clse, rcl, "chunk lse")
     assert_close(out, ro, TOL["fp8_e4m3"], "out")
     assert_lse(lse, rl, "lse")
+
+
+def test_mla_scores_far_above_the_first_tile(gpu):
+    """The fp8 latent kernel exponentiates against each row's first-tile
+    maximum and restarts the partition with a raised reference when a later
+    score exceeds it by more than 2^16; these keys force that: request 0 has
+    one key aligned with head 0's query in its fourth tile (one restart),
+    request 1 one in its second tile and a larger one in its eighth (two
+    restarts), request 2 is untouched. Against the one-softmax definition."""
+    pre_lens, suf_lens = [512, 300, 700], [40, 0, 64]
+    pre = W.random_batch(3121, batch=3, page_size=64, num_q_heads=128, num_kv_heads=1,
+                         head_dim=576, head_dim_v=512, kv_dtype="fp8_e4m3", q_dtype="bf16",
+                         min_len=0, max_len=0, partition_tokens=512, lens=pre_lens, latent=True)
+    suf = W.random_batch(3122, batch=3, page_size=64, num_q_heads=128, num_kv_heads=1,
+                         head_dim=576, head_dim_v=512, kv_dtype="bf16", q_dtype="bf16",
+                         min_len=0, max_len=0, partition_tokens=64, lens=suf_lens, latent=True)
+    suf.q = pre.q
+    suf.sm_scale = pre.sm_scale
+    qf = (pre.q.astype(np.uint32) << 16).view(np.float32)  # bf16 bits -> f32
+    for b, t, amp in ((0, 100, 1.0), (1, 40, 0.8), (1, 250, 2.0)):
+        row = int(pre.indices[pre.indptr[b] + t // 64])
+        key = amp * np.sign(qf[b, 0]).astype(np.float32)
+        pre.k_pool[row, 0, t % 64] = W._fp8_bits(key, pre.k_scale)
+    share = W.MlaShare(prefix=pre, suffix=suf, chunk_tokens=512)
+    out, lse, _, _, _ = run_chunked(gpu, share, staged=False)
+    fo, fl = omla.mla_flat(share)
+    # the planted keys do dominate head 0 of the requests that hold them
+    s = fl[:2, 0] - np.delete(fl[:2], 0, axis=1).max(axis=1)
+    assert np.all(s > 10), s
+    assert_close(out, fo, TOL["fp8_e4m3"], "out")
+    assert_lse(lse, fl, "lse")
