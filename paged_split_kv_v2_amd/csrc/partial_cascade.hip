@@ -23,12 +23,14 @@ namespace {
 
 constexpr int kL0Waves = 4;  // level-0 body: 4 waves x 16 stacked query rows
 constexpr int kL0Stages = 2;  // level-0 LDS ring: two 32-token stages
-// Level-0 rows with ordinary (cached) loads: a step's unique bytes (0.28 GB
-// on the 72-request shared-prefix step) largely fit the last-level cache, and
-// non-temporal fetches there cost 51.4 -> 54.1 us when steps run back to
-// back. (The level-1 body keeps its non-temporal loads: cached ones gained
-// nothing back to back and cost 67.5 -> 72.3 us with a cold cache.)
-constexpr bool kL0Streaming = false;
+// Level-0 rows with non-temporal (streaming) loads, like level 1. Timed on
+// the step a model sees, after a read that evicts the last-level cache
+// (other layers run between two steps of one layer), the 72-request
+// shared-prefix step takes 65.7 us with them against 68.0 us with cached
+// level-0 loads; only when steps of one layer run back to back, so that the
+// step's 0.28 GB of unique bytes partly stay in the 256 MB last-level
+// cache, do cached loads win (58.6 against 61.9 us).
+constexpr bool kL0Streaming = true;
 static_assert(64 * kL0Waves == kThreads, "both bodies run on 256-thread workgroups");
 
 // Three workgroups per compute unit: the level-1 body alone fits three (156
