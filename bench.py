@@ -472,11 +472,26 @@ def gate_arm(args, torch, pdk, b, pool, q, flat_plan, dev):
     def lookup():
         cache.get(b.indptr, b.indices, b.kv_len, b.page_size, gate_params)
 
-    arms = {}
-    for name, pre in (("flat_only", []), ("detect_then_flat", [detect]),
-                      ("plan_cache_then_flat", [lookup])):
-        region_ms, _ = time_steps(torch, pre + parts, args.steps, args.warmup, args.reps)
-        arms[name] = stats_of([m * 1000 for m in region_ms])
+    # the arms' regions interleave (the order rotating from rep to rep), so
+    # that clock and thermal drift over the run falls on every arm alike
+    spec = (("flat_only", []), ("detect_then_flat", [detect]),
+            ("plan_cache_then_flat", [lookup]))
+    for _, pre in spec:
+        for _ in range(args.warmup):
+            for f in pre + parts:
+                f()
+    region_us = {name: [] for name, _ in spec}
+    for rep in range(args.reps):
+        for k in range(len(spec)):
+            name, pre = spec[(rep + k) % len(spec)]
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                for f in pre + parts:
+                    f()
+            torch.cuda.synchronize()
+            region_us[name].append((time.perf_counter() - t0) * 1e6 / args.steps)
+    arms = {name: stats_of(v) for name, v in region_us.items()}
     t0 = time.perf_counter()
     for _ in range(50):
         detect()

@@ -35,17 +35,31 @@ static_assert(64 * kL0Waves == kThreads, "both bodies run on 256-thread workgrou
 
 // Three workgroups per compute unit: the level-1 body alone fits three (156
 // registers), and with a two-stage ring the level-0 body keeps its
-// accumulators in the same budget (no accumulator registers), 47 KB of LDS
-// each. A deeper ring would hold more of level 0 in flight but costs the
-// third workgroup, which level 1 - most of the bytes - needs more (measured
-// on the batch-72 shared-prefix step: 57 against 64 us).
+// accumulators in the same budget (160 registers, no accumulator registers).
+// The level-1 body's LDS (the cross-wave merge and its page ids) overlays the
+// first ring stage, since no workgroup runs both bodies: 34 KB per
+// workgroup. A three-stage ring then also fits three workgroups (50 KB), but
+// measured on the batch-72 shared-prefix step it is no faster (62.5 against
+// 61.0 us per cold step): alone in the grid, level 0 takes 33 us and level 1
+// 42 us, so the level-1 workgroups, which hold most of the bytes, set the
+// pace, not the level-0 ring's depth.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void cascade_partial_kernel(const PartialArgs a0, const PartialArgs a1, const int blocks0) {
+  constexpr int kStage = 2 * 32 * 128;  // one K + V tile of 32 tokens (bf16 elements)
+  __shared__ __align__(16) uint16_t st0[kStage];
+  __shared__ __align__(16) uint16_t st1[kStage];
+  __shared__ __align__(16) uint16_t st2[kL0Stages > 2 ? kStage : 8];
+  __shared__ __align__(16) uint16_t st3[kL0Stages > 3 ? kStage : 8];
+  __shared__ int pid0[kMaxPagesD];
+  using L1Lds = ValuLds<4, 128>;
+  static_assert(sizeof(L1Lds) <= sizeof(st0), "level-1 LDS overlays the first ring stage");
   const int bid = blockIdx.x;
   if (bid < blocks0)
-    partial_dma_body<128, 32, kL0Stages, kL0Waves, true, kL0Streaming>(a0, bid);
-  else
-    partial_valu_body<KV_BF16, PDK_BF16, 128, 4, true, false>(a1, bid - blocks0);
+    partial_dma_body<128, 32, kL0Stages, kL0Waves, true, kL0Streaming>(
+        a0, bid, DmaLds{st0, st1, st2, st3, pid0});
+  else  // a level-1 workgroup never runs the level-0 body: its LDS is free
+    partial_valu_body<KV_BF16, PDK_BF16, 128, 4, true, false>(
+        a1, bid - blocks0, *reinterpret_cast<L1Lds*>(st0));
 }
 
 }  // namespace

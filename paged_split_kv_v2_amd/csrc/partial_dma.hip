@@ -22,7 +22,12 @@ namespace {
 template <int D, int TT, int NS, int NW, bool SPLIT>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void partial_dma_kernel(const PartialArgs a) {
-  partial_dma_body<D, TT, NS, NW, SPLIT, true>(a, blockIdx.x);
+  __shared__ __align__(16) uint16_t st0[2 * TT * D];
+  __shared__ __align__(16) uint16_t st1[2 * TT * D];
+  __shared__ __align__(16) uint16_t st2[(NS > 2) ? 2 * TT * D : 8];
+  __shared__ __align__(16) uint16_t st3[(NS > 3) ? 2 * TT * D : 8];
+  __shared__ int pid[kMaxPagesD];
+  partial_dma_body<D, TT, NS, NW, SPLIT, true>(a, blockIdx.x, DmaLds{st0, st1, st2, st3, pid});
 }
 
 typedef void (*DmaFn)(const PartialArgs);

@@ -69,11 +69,25 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
+// The LDS of the matrix-core body, declared by the kernel that runs it: the
+// ring stages (2*TT*D elements each; stages past NS are not used), each its
+// own LDS object, and the partition's page ids (kMaxPagesD). Separate
+// objects let the compiler's wait insertion tell the stages apart: an LDS
+// read of one stage does not wait for global->LDS loads into another.
+struct DmaLds {
+  uint16_t* st0;
+  uint16_t* st1;
+  uint16_t* st2;
+  uint16_t* st3;
+  int* pid;
+};
+
 // The work of one workgroup of 64 * NW threads: `block` is its index in the
 // grid of its launch (the decomposition below is over that index). NT: the
 // K/V fetches are non-temporal (streaming) loads.
 template <int D, int TT, int NS, int NW, bool SPLIT, bool NT>
-__device__ __forceinline__ void partial_dma_body(const PartialArgs& a, const int block) {
+__device__ __forceinline__ void partial_dma_body(const PartialArgs& a, const int block,
+                                                 const DmaLds& lds) {
   constexpr int KS = D / 32;                 // k-steps of S^T
   constexpr int TB = TT / 16;                // 16-token blocks per tile
   constexpr int KB = TT / 32;                // 32-token PV steps per tile
@@ -85,11 +99,11 @@ __device__ __forceinline__ void partial_dma_body(const PartialArgs& a, const int
   static_assert(NI % NW == 0 && TT % 32 == 0 && NS >= 2 && NS <= 4, "tile shapes");
   static_assert((NS - 2) * NIW < 64, "vmcnt range");
 
-  __shared__ __align__(16) uint16_t st0[2 * TT * D];
-  __shared__ __align__(16) uint16_t st1[2 * TT * D];
-  __shared__ __align__(16) uint16_t st2[(NS > 2) ? 2 * TT * D : 8];
-  __shared__ __align__(16) uint16_t st3[(NS > 3) ? 2 * TT * D : 8];
-  __shared__ int sm_pid[kMaxPagesD];
+  uint16_t* const st0 = lds.st0;
+  uint16_t* const st1 = lds.st1;
+  uint16_t* const st2 = lds.st2;
+  uint16_t* const st3 = lds.st3;
+  int* const sm_pid = lds.pid;
 
   const int n_rt = (a.max_rows + 16 * NW - 1) / (16 * NW);
   int unit, rt;
@@ -207,24 +221,37 @@ __device__ __forceinline__ void partial_dma_body(const PartialArgs& a, const int
   const int v_tok = 4 * q4 + (r16 >> 2);
   const int v_sw = dswz(v_tok);            // also tokens v_tok + 16: same t mod 16
   const int v_sub = (lane & 3);            // 4-dim piece within the 16 dims
+  // Each lane's V^T fragment offset (elements, within a 32-token block) for
+  // the 16-dim output block db is chunk 2db + v_sub/2 of token v_tok, i.e.
+  // v_base + 16 (db ^ v_w) (the swizzle's low bit only moves v_sub/2). Kept
+  // to this form, a fragment address is the stage, the tile's V half, v_base,
+  // the db term and a constant: few enough address steps that the compiler
+  // ties every transposing load to its stage. (With one more step it loses
+  // that link, and such a load waits for every global->LDS load in flight,
+  // the next tiles' fetches included.)
+  const int v_base = v_tok * D + 8 * ((v_sub >> 1) ^ (v_sw & 1)) + 4 * (v_sub & 1);
+  const int v_w = v_sw >> 1;
 
   const int n_tiles = (end > start) ? (end - start + TT - 1) / TT : 0;
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): query fragments have landed
   __syncthreads();                     // page ids visible
+  // Every tile issues exactly one fetch, also past the last tile: such a
+  // fetch reads the last token's rows (every lane the same 256 bytes of K and
+  // of V) into the free stage, which nothing reads again. With a fetch on
+  // every path, tile i's bytes are always followed by exactly NS - 2 later
+  // fetches when tile i starts, so one constant wait count covers every
+  // path; a fetch skipped on some paths makes the compiler's own wait
+  // insertion assume the worst and wait for every fetch in flight.
+  if (n_tiles > 0) {
 #pragma unroll
-  for (int j = 0; j < NS - 1; ++j)
-    if (j < n_tiles) fetch(j, stage(j));
+    for (int j = 0; j < NS - 1; ++j) fetch(j, stage(j));
+  }
 
   auto tile = [&](int i, uint16_t* buf, uint16_t* next) {
-    // tile i has landed once at most min(NS-2, n_tiles-1-i) later tiles are
-    // still in flight
-    const int later = min(NS - 2, n_tiles - 1 - i);
-    if (later >= 2) wait_vm<(NS >= 4 ? 2 * NIW : 0)>();
-    else if (later == 1) wait_vm<NIW>();
-    else wait_vm<0>();
+    wait_vm<(NS - 2) * NIW>();  // tile i has landed (this wave's part)
     if (NW > 1) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     // every wave is past tile i - 1: its stage takes tile i + NS - 1
-    if (i + NS - 1 < n_tiles) fetch(i + NS - 1, next);
+    fetch(i + NS - 1, next);
     // a wave without live rows only fetches and keeps the barriers
     if (!live_wave) return;
     const int t0 = start + i * TT;
@@ -311,9 +338,9 @@ __device__ __forceinline__ void partial_dma_body(const PartialArgs& a, const int
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         // chunk 2db + v_sub/2 of tokens 32kb + v_tok and 32kb + 16 + v_tok
-        const int qc = 2 * db + (v_sub >> 1);
-        const uint16_t* p0 = vt + (32 * kb + v_tok) * D + 8 * (qc ^ v_sw) + 4 * (v_sub & 1);
-        const uint16_t* p1 = vt + (32 * kb + 16 + v_tok) * D + 8 * (qc ^ v_sw) + 4 * (v_sub & 1);
+        const int vo = v_base + 16 * (db ^ v_w);
+        const uint16_t* p0 = vt + vo + 32 * kb * D;
+        const uint16_t* p1 = vt + vo + (32 * kb + 16) * D;
         const u32x2_t v0 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p0));
         const u32x2_t v1 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p1));
         const bf16x8_t vf = as_bf16x8(u32x4_t{v0[0], v0[1], v1[0], v1[1]});
@@ -325,14 +352,24 @@ __device__ __forceinline__ void partial_dma_body(const PartialArgs& a, const int
 
   // ring of NS stages: tile i computes from stage i % NS, and tile i + NS - 1
   // is fetched into the stage tile i - 1 used (free once every wave passed
-  // the barrier of tile i)
-  for (int i0 = 0; i0 < n_tiles; i0 += NS) {
+  // the barrier of tile i). The loop runs whole rounds of NS tiles and the
+  // last n_tiles % NS tiles follow it, each only after the one before, so
+  // that every path into a tile carries the same fetches in flight (a round
+  // cut short inside the loop would give the loop's back edge such a path).
+  int i0 = 0;
+  for (; i0 + NS <= n_tiles; i0 += NS) {
 #pragma unroll
-    for (int k = 0; k < NS; ++k) {
-      const int i = i0 + k;
-      if (i < n_tiles) tile(i, stage(k), stage((k + NS - 1) % NS));
+    for (int k = 0; k < NS; ++k) tile(i0 + k, stage(k), stage((k + NS - 1) % NS));
+  }
+  const int rest = n_tiles - i0;
+  if (rest > 0) {
+    tile(i0, stage(0), stage(NS - 1));
+    if (NS > 2 && rest > 1) {
+      tile(i0 + 1, stage(1), stage(0));
+      if (NS > 3 && rest > 2) tile(i0 + 2, stage(2), stage(1));
     }
   }
+  wait_vm<0>();  // no global->LDS load outlives the workgroup
 
   // row sum across the lane groups, then the normalized partial and its LSE
   float l = run_l;

@@ -10,7 +10,8 @@ namespace {
 
 template <int KT, int QT, int D, int GM, bool UNIF, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void partial_valu_kernel(const PartialArgs a) {
-  partial_valu_body<KT, QT, D, GM, UNIF, CAUSAL>(a, blockIdx.x);
+  __shared__ ValuLds<GM, D> lds;
+  partial_valu_body<KT, QT, D, GM, UNIF, CAUSAL>(a, blockIdx.x, lds);
 }
 
 typedef void (*KernelFn)(const PartialArgs);

@@ -279,10 +279,23 @@ __device__ __forceinline__ void valu_finish(const float (&sm_acc)[4][GM][D],
   }
 }
 
+// The LDS a workgroup of the vector body uses: the cross-wave merge of the
+// row-group states and the partition's page ids. The kernel that runs the
+// body owns it (a kernel running two bodies in disjoint blocks can overlay
+// it on the other body's LDS).
+template <int GM, int D>
+struct ValuLds {
+  float acc[4][GM][D];
+  float m[4][GM];
+  float l[4][GM];
+  int pid[kMaxPartPages];
+};
+
 // The work of one workgroup of 256 threads: `block` is its index in the
 // grid of its launch (the decomposition below is over that index).
 template <int KT, int QT, int D, int GM, bool UNIF, bool CAUSAL>
-__device__ __forceinline__ void partial_valu_body(const PartialArgs& a, const int block) {
+__device__ __forceinline__ void partial_valu_body(const PartialArgs& a, const int block,
+                                                  ValuLds<GM, D>& lds) {
   constexpr int E = D / 16;                          // elements per lane
   constexpr int NU = E * (KT == KV_F32 ? 4 : 2) / 4; // 32-bit words per lane per row
   constexpr bool kDot2 = (KT == KV_BF16 && QT == PDK_BF16);
@@ -291,10 +304,10 @@ __device__ __forceinline__ void partial_valu_body(const PartialArgs& a, const in
   constexpr int T = TokPerRowGroup<GM, E>::value;
   constexpr int kStep = 16 * T;  // tokens per step of the workgroup
 
-  __shared__ float sm_acc[4][GM][D];
-  __shared__ float sm_m[4][GM];
-  __shared__ float sm_l[4][GM];
-  __shared__ int sm_pid[kMaxPartPages];
+  float (&sm_acc)[4][GM][D] = lds.acc;
+  float (&sm_m)[4][GM] = lds.m;
+  float (&sm_l)[4][GM] = lds.l;
+  int (&sm_pid)[kMaxPartPages] = lds.pid;
 
   const int n_tiles = (a.max_rows + GM - 1) / GM;
   int unit, tile;
