@@ -587,7 +587,7 @@ def mla_arm(args, torch, pdk, share, dev):
                          "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                          "traffic": traffic_record("partial_latent.hip"),
                          "mfma_busy": mfma_busy_record("partial_latent.hip"),
-                         "kernel": "partial_latent_kernel<576,512,fp8>",
+                         "kernel": "partial_latent_fp8_kernel<576,512>",
                          "kernel_us": round(pus, 2), "kernel_us_reps": stats_of(part_us),
                          "flops_per_launch": flops_part}}
 
@@ -881,7 +881,7 @@ def bench_flat_mt(args, torch, pdk, W, dev, b, T=4):
                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                          "traffic": traffic_record("partial_dma.hip",
                                                    f"llama3_8b_flat_{T}_token_causal_step"),
-                         "kernel": f"partial_dma_kernel<128,32,4,4> ({T * b.group} rows per "
+                         "kernel": f"partial_dma_kernel<128,32,3 stages,4 waves> ({T * b.group} rows per "
                                    "KV head)",
                          "kernel_us": round(pus, 2), "bytes_per_launch": alg},
             "kernels_us": {"partials": stats_of(t_part), "merge": stats_of(t_merge)}}
@@ -947,7 +947,7 @@ def bench_mla_mt(args, torch, pdk, W, dev, share, T=4):
                          "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                          "traffic": traffic_record("partial_latent.hip",
                                                    "mla_decode_share_b32_ctx16384_fp8_4_token_step"),
-                         "kernel": f"partial_latent_kernel<576,512,fp8> ({T} tokens x {Hq} heads)",
+                         "kernel": f"partial_latent_fp8_kernel<576,512> ({T} tokens x {Hq} heads)",
                          "kernel_us": round(pus, 2), "flops_per_launch": flops_part}}
 
 

@@ -9,18 +9,17 @@ namespace pdk {
 
 namespace {
 
-// Four workgroups per compute unit: with a two-stage ring the body fits 128
-// registers (accumulators included) and 35 KB of LDS. Measured on the 4-token
-// Llama-3-8B step (16 rows per KV head): 235 us here, 273 us with a
-// four-stage ring at two workgroups per compute unit, 238 us with three
-// stages at three; occupancy hides the per-tile barrier and products better
-// than a deeper ring hides memory latency.
+// Three workgroups per compute unit, each with a three-stage ring (160
+// registers, accumulators included, and 50 KB of LDS): two tiles are in
+// flight while one is multiplied. Measured on the 4-token Llama-3-8B step
+// (16 rows per KV head): 217 us, against 221 us for a two-stage ring at four
+// workgroups per compute unit (128 registers, one spilled) or at three.
 //
 // The K/V rows are fetched with non-temporal loads, as the vector kernel reads
 // them: 4-token Llama-3-8B step 233 -> 220 us (1.2 GB, far more than the
 // last-level cache holds, so caching them only evicts other data).
 template <int D, int TT, int NS, int NW, bool SPLIT>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void partial_dma_kernel(const PartialArgs a) {
   __shared__ __align__(16) uint16_t st0[2 * TT * D];
   __shared__ __align__(16) uint16_t st1[2 * TT * D];
@@ -46,7 +45,7 @@ int launch_partial_dma(const PartialArgs& a, hipStream_t stream, bool* handled) 
       a.Dv != 128 || a.p_shift < 2 || a.max_rows < 16)
     return PDK_OK;
   const int nw = 4;
-  DmaFn fn = partial_dma_kernel<128, 32, 2, 4, true>;
+  DmaFn fn = partial_dma_kernel<128, 32, 3, 4, true>;
   if (a.S / a.P + 1 > kMaxPagesD)
     return fail(PDK_ERR_UNSUPPORTED, "partition of %d tokens spans more than %d pages", a.S,
                 kMaxPagesD - 1);
