@@ -442,22 +442,31 @@ __device__ __forceinline__ void partial_valu_body(const PartialArgs& a, const in
     valu_step<KT, QT, D, GM, CAUSAL>(X, qw, lim, a.scale_log2, run_m, run_l, acc);
   };
 
-  // two register tiles: the next step's rows are requested before the
-  // current step is computed
+  // Two register tiles: the next step's rows are requested before the
+  // current step is computed. The loop runs whole pairs of steps and the
+  // last one or two steps follow it, so that every path into a step's
+  // computation carries exactly the next step's loads in flight. (With the
+  // next step's load skipped on some path, as a loop that tests for the
+  // last step inside would have, the compiler's wait counting assumes the
+  // worst and waits for every load in flight, the next step's included.)
+  const int n_steps = (end > start) ? (end - start + kStep - 1) / kStep : 0;
   Tile<NU, T> A, B;
-  int t0 = start;
-  if (t0 < end) load_step(t0, A);
-  while (t0 < end) {
-    const bool more1 = t0 + kStep < end;  // uniform
-    if (more1) load_step(t0 + kStep, B);
-    compute_step(A);
-    t0 += kStep;
-    if (!more1) break;
-    const bool more2 = t0 + kStep < end;
-    if (more2) load_step(t0 + kStep, A);
-    compute_step(B);
-    t0 += kStep;
-    if (!more2) break;
+  if (n_steps > 0) {
+    load_step(start, A);
+    int s = 0;
+    for (; s + 2 < n_steps; s += 2) {
+      load_step(start + (s + 1) * kStep, B);
+      compute_step(A);
+      load_step(start + (s + 2) * kStep, A);
+      compute_step(B);
+    }
+    if (s + 1 < n_steps) {
+      load_step(start + (s + 1) * kStep, B);
+      compute_step(A);
+      compute_step(B);
+    } else {
+      compute_step(A);
+    }
   }
 
   valu_wave_merge(run_m, run_l, acc);
