@@ -352,9 +352,9 @@ __device__ __forceinline__ void partial_dma_body(const PartialArgs& a, const int
 
   // ring of NS stages: tile i computes from stage i % NS, and tile i + NS - 1
   // is fetched into the stage tile i - 1 used (free once every wave passed
-  // the barrier of tile i). The loop runs whole rounds of NS tiles and the
+  // the barrier of tile i). The loop runs whole cycles of NS tiles and the
   // last n_tiles % NS tiles follow it, each only after the one before, so
-  // that every path into a tile carries the same fetches in flight (a round
+  // that every path into a tile carries the same fetches in flight (a cycle
   // cut short inside the loop would give the loop's back edge such a path).
   int i0 = 0;
   for (; i0 + NS <= n_tiles; i0 += NS) {
