@@ -485,17 +485,23 @@ void partial_latent_kernel(const PartialArgs a) {
 // dependent products) interleaved with O^T of tile i - 1 (32 products on 16
 // independent accumulators, k-step major), so that the matrix core always
 // has an independent product to start; the dequantization of tile i + 1
-// and the fetch of tile i + 2 spread over the same loop; then the softmax
-// of tile i. The S^T products are written as inline asm with VGPR operands
-// and the O^T products with accumulation-register operands: the compiler
-// otherwise gives every product's accumulator the same register file and
-// has no room for both.
-// Measured (32 requests x 16384 fp8 tokens, 2048-token partitions): 165 us
-// per launch against 195 us for the 8-wave kernel above; with the matrix
-// cores 38% busy by counter, LDS 24% busy, no bank conflicts. Timing
-// variants put the products alone at about 62% of the matrix-core rate
-// and show the dequantization and the softmax not hidden behind them: with
-// one wave per SIMD no other wave fills the issue slots they take.
+// (two vector operations after each product) and the fetch of tile i + 2
+// spread over the same loop; then the softmax of tile i. The S^T products
+// are written as inline asm with VGPR operands and the O^T products with
+// accumulation-register operands: the compiler otherwise gives every
+// product's accumulator the same register file and has no room for both.
+// The query fragments are fetched first, so that their issue (36 loads of
+// 32 rows each) overlaps the page-table reads.
+// Measured (32 requests x 16384 fp8 tokens, 2048-token partitions): about
+// 170 us per launch against 195 us for the 8-wave kernel above; with the
+// matrix cores 36% busy by counter, LDS 23% busy, no bank conflicts. Cycle
+// stamps (s_memtime) per workgroup: prologue 8 us, tile loop 134 us, the
+// partial's stores 14 us; the clock under this load is 1.8-2.0 GHz, not
+// 2.4. An interval takes about 4,100 cycles against 2,176 of products:
+// the softmax (about 560 cycles) runs with the matrix core idle, and the
+// LDS stores of the dequantized tile and the vector operations cost about
+// 450 and 300 cycles of the products loop. With one wave per SIMD no other
+// wave fills the issue slots they take.
 // Softmax reference: a row's scores are exponentiated against a fixed
 // reference, its maximum over the first tile it sees, and the accumulators
 // are never rescaled (a VALU rescale of accumulator registers costs the
@@ -539,6 +545,14 @@ void partial_latent_fp8_kernel(const PartialArgs a) {
   const int n_tiles = (a.max_rows + ROWS - 1) / ROWS;
   int unit, tile;
   xcd_unit_tile(blockIdx.x, n_tiles, unit, tile);
+  {
+    // Workgroups are dealt to the 8 XCDs round robin by block index. With
+    // one tile per unit and a unit count divisible by 8, XCD x takes the
+    // consecutive units [x units/8, (x+1) units/8): a request's partitions
+    // (consecutive units reading the same query rows) then share one L2.
+    const int units = a.num_parts * a.Hkv;
+    if (n_tiles == 1 && (units & 7) == 0) unit = (blockIdx.x & 7) * (units >> 3) + (blockIdx.x >> 3);
+  }
   if (unit >= a.num_parts * a.Hkv) return;  // grid padding (uniform)
   const int h = unit % a.Hkv;
   const int r = unit / a.Hkv;
@@ -563,34 +577,15 @@ void partial_latent_fp8_kernel(const PartialArgs a) {
   const int row0 = tile * ROWS;
   if (row0 >= nrows) return;  // uniform
 
-  int page0, start, end;
-  part_range(a, b, p, page0, start, end);
-  // causal rows: the tile loop stops at the last owned row's end; every
-  // owned row sees at least the positions below end_lo (uniform)
-  const int end_lo = min(end, visible_end(a, b, row0 / a.G));
-  end = min(end, visible_end(a, b, (min(row0 + ROWS, nrows) - 1) / a.G));
-  const int shift = a.p_shift;
-  const int pmask = a.P - 1;
-  const int pg_first = start >> shift;
-  if (end > start) {
-    const int n_pg = ((end - 1) >> shift) - pg_first + 1;
-    for (int i = tid; i < n_pg; i += NT) {
-      const int pid = a.indices[page0 + pg_first + i];
-      // an id outside the pool reads row 0 (see part_range)
-      sm_pid[i] = ((unsigned)pid < (unsigned)a.num_blocks) ? pid : 0;
-    }
-  }
-  if (tid == 0) sm_restart = 0;
-
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int hf = lane >> 5;    // lane half
   const int n32 = lane & 31;   // query row of the wave (MFMA column) / token of a K read
   const int my_row = row0 + RW * wave + n32;
   const bool live_wave = row0 + RW * wave < nrows;  // uniform over the wave
-  const int my_end = min(end, visible_end(a, b, min(my_row, nrows - 1) / a.G));
 
-  // Q^T fragments: lane -> row n32, dims 16ks + 8hf + 0..7
+  // Q^T fragments: lane -> row n32, dims 16ks + 8hf + 0..7. Issued before
+  // the page-table reads below, which their issue then overlaps.
   u32x4_t qf[KS];
   {
     int qb = b, head = 0;
@@ -609,6 +604,26 @@ void partial_latent_fp8_kernel(const PartialArgs a) {
       qf[ks] = live ? x : u32x4_t{0u, 0u, 0u, 0u};
     }
   }
+
+  int page0, start, end;
+  part_range(a, b, p, page0, start, end);
+  // causal rows: the tile loop stops at the last owned row's end; every
+  // owned row sees at least the positions below end_lo (uniform)
+  const int end_lo = min(end, visible_end(a, b, row0 / a.G));
+  end = min(end, visible_end(a, b, (min(row0 + ROWS, nrows) - 1) / a.G));
+  const int shift = a.p_shift;
+  const int pmask = a.P - 1;
+  const int pg_first = start >> shift;
+  if (end > start) {
+    const int n_pg = ((end - 1) >> shift) - pg_first + 1;
+    for (int i = tid; i < n_pg; i += NT) {
+      const int pid = a.indices[page0 + pg_first + i];
+      // an id outside the pool reads row 0 (see part_range)
+      sm_pid[i] = ((unsigned)pid < (unsigned)a.num_blocks) ? pid : 0;
+    }
+  }
+  if (tid == 0) sm_restart = 0;
+  const int my_end = min(end, visible_end(a, b, min(my_row, nrows - 1) / a.G));
 
   const char* kbase = reinterpret_cast<const char*>(a.k) + (size_t)h * a.k_hstride;
   const long long kb_stride = a.k_bstride;
@@ -738,22 +753,65 @@ void partial_latent_fp8_kernel(const PartialArgs a) {
     for (int i = 0; i < KP; ++i) kf[i] = kread(i);
 #pragma unroll
     for (int i = 0; i < VP; ++i) vf[i] = vread(i);
+    // Dequantization of unit k: 16 vector operations (the unit's two 4-code
+    // words in turn: both halves widened to binary32, exactly; four products
+    // with the scale; two RNE roundings to bf16 pairs: RNE_bf16(RNE_f32(x *
+    // scale)), the instructions fp8x4_dequant_bf16 compiles to), spread
+    // evenly over the products of the unit's steps. Each is its own asm
+    // statement so that it stays where it is put: as ordinary code the
+    // compiler gathers a unit's operations between two products, and the
+    // matrix core then waits for them.
+    f32x2_t dq_lo, dq_hi;
+    float dq_m[4];
+    uint32_t dq_w[4];
+    const float scl = a.k_scale;
+    auto dq_op = [&](int k, int j) {
+      const uint32_t x = F[k][j >> 3];
+      switch (j & 7) {
+        case 0: asm volatile("v_cvt_pk_f32_fp8_e32 %0, %1" : "=v"(dq_lo) : "v"(x)); break;
+        case 1: asm volatile("v_cvt_pk_f32_fp8_sdwa %0, %1 src0_sel:WORD_1" : "=v"(dq_hi) : "v"(x)); break;
+        case 2: asm volatile("v_mul_f32_e32 %0, %1, %2" : "=v"(dq_m[0]) : "s"(scl), "v"(dq_lo[0])); break;
+        case 3: asm volatile("v_mul_f32_e32 %0, %1, %2" : "=v"(dq_m[1]) : "s"(scl), "v"(dq_lo[1])); break;
+        case 4: asm volatile("v_mul_f32_e32 %0, %1, %2" : "=v"(dq_m[2]) : "s"(scl), "v"(dq_hi[0])); break;
+        case 5: asm volatile("v_mul_f32_e32 %0, %1, %2" : "=v"(dq_m[3]) : "s"(scl), "v"(dq_hi[1])); break;
+        case 6:
+          asm volatile("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(dq_w[2 * (j >> 3)]) : "v"(dq_m[0]), "v"(dq_m[1]));
+          break;
+        default:
+          asm volatile("v_cvt_pk_bf16_f32 %0, %1, %2"
+                       : "=v"(dq_w[2 * (j >> 3) + 1]) : "v"(dq_m[2]), "v"(dq_m[3]));
+      }
+    };
+    // products in steps [t0, t1), and unit k's share of its operations for
+    // the idx-th product of its steps
+    auto n_products = [](int t0, int t1) {
+      int n = 0;
+      for (int t = t0; t < t1; ++t) n += (t < KS) + (t < NPV);
+      return n;
+    };
+    auto dq_share = [&](int st, int slot) {
+      const int k = st / CONV_EVERY;
+      if (k >= UPL) return;
+      const int t0 = k * CONV_EVERY;
+      const int n = n_products(t0, t0 + CONV_EVERY);
+      const int idx = n_products(t0, st) + slot;
+      for (int j = 16 * idx / n; j < 16 * (idx + 1) / n; ++j) dq_op(k, j);
+    };
 #pragma unroll
     for (int st = 0; st < STEPS; ++st) {
       if (st < KS) {
         if (st + KP < KS) kf[(st + KP) % (KP + 1)] = kread(st + KP);
         qk_step(st, kf[st % (KP + 1)], qf[st], s);
+        dq_share(st, 0);
       }
       if (st < NPV) {
         if (st + VP < NPV) vf[(st + VP) % (VP + 1)] = vread(st + VP);
         pv_step(st, vf[st % (VP + 1)], pb[st / DB], acc[st % DB]);
+        dq_share(st, st < KS ? 1 : 0);
       }
       if (st % CONV_EVERY == CONV_EVERY - 1 && st / CONV_EVERY < UPL) {
         const int k = st / CONV_EVERY;
-        uint32_t w[4];
-        fp8x4_dequant_bf16(F[k][0], a.k_scale, w[0], w[1]);
-        fp8x4_dequant_bf16(F[k][1], a.k_scale, w[2], w[3]);
-        *reinterpret_cast<u32x4_t*>(dst + 128 * k) = u32x4_t{w[0], w[1], w[2], w[3]};
+        *reinterpret_cast<u32x4_t*>(dst + 128 * k) = u32x4_t{dq_w[0], dq_w[1], dq_w[2], dq_w[3]};
         F[k] = *reinterpret_cast<const u32x2_t*>(src + 64 * k);
       }
     }
