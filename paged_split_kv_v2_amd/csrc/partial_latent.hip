@@ -482,10 +482,11 @@ void partial_latent_kernel(const PartialArgs a) {
 // (RNE_bf16(f32(x) * scale)) into a bf16 LDS buffer one interval later. No
 // global->LDS loads, so no LDS access waits for a fetch.
 // Interval i (one barrier; three buffers): the S^T chain of tile i (36
-// dependent products) interleaved with O^T of tile i - 1 (32 products on 16
-// independent accumulators, k-step major), so that the matrix core always
-// has an independent product to start; the dequantization of tile i + 1
-// (two vector operations after each product) and the fetch of tile i + 2
+// dependent products; gfx950 issues such a chain at the full rate)
+// interleaved with O^T of tile i - 1 (32 products on 16 independent
+// accumulators, k-step major), which spreads the K and V^T reads evenly;
+// the dequantization of tile i + 1 (two vector operations after each
+// product) and the fetch of tile i + 2
 // spread over the same loop; then the softmax of tile i. The S^T products
 // are written as inline asm with VGPR operands and the O^T products with
 // accumulation-register operands: the compiler otherwise gives every
@@ -711,11 +712,10 @@ void partial_latent_fp8_kernel(const PartialArgs a) {
 
   // One interval's products: S^T of tile `cur` (a chain of KS dependent
   // MFMAs) interleaved with O^T += V^T . P^T of the tile before it (2 DB
-  // MFMAs on DB independent accumulators, k-step major), so that the matrix
-  // core always has an independent product to start while the S^T chain
-  // waits for its previous step; the dequantization of the next tile and
-  // the fetch of the one after it are spread over the same loop, one unit
-  // every few steps. K fragments are read KP steps ahead, V^T fragments VP
+  // MFMAs on DB independent accumulators, k-step major), which spreads the
+  // K and V^T reads evenly; the dequantization of the next tile and the
+  // fetch of the one after it are spread over the same loop, one unit every
+  // few steps. K fragments are read KP steps ahead, V^T fragments VP
   // steps ahead, into rings of registers (deeper rings measured no faster).
   // The dequantization and fetch always run (past the last tile they repeat
   // it: same bytes, unused buffer).
