@@ -802,6 +802,15 @@ void partial_latent_fp8_kernel(const PartialArgs a) {
       if (st < KS) {
         if (st + KP < KS) kf[(st + KP) % (KP + 1)] = kread(st + KP);
         qk_step(st, kf[st % (KP + 1)], qf[st], s);
+        // the previous unit's LDS store and the next fetch into its
+        // registers, one product after the unit's last operation, so that
+        // the store does not wait on it (the next unit writes dq_w only in
+        // its second step)
+        if (st % CONV_EVERY == 0 && st > 0 && st / CONV_EVERY - 1 < UPL) {
+          const int k = st / CONV_EVERY - 1;
+          *reinterpret_cast<u32x4_t*>(dst + 128 * k) = u32x4_t{dq_w[0], dq_w[1], dq_w[2], dq_w[3]};
+          F[k] = *reinterpret_cast<const u32x2_t*>(src + 64 * k);
+        }
         dq_share(st, 0);
       }
       if (st < NPV) {
@@ -809,11 +818,12 @@ void partial_latent_fp8_kernel(const PartialArgs a) {
         pv_step(st, vf[st % (VP + 1)], pb[st / DB], acc[st % DB]);
         dq_share(st, st < KS ? 1 : 0);
       }
-      if (st % CONV_EVERY == CONV_EVERY - 1 && st / CONV_EVERY < UPL) {
-        const int k = st / CONV_EVERY;
-        *reinterpret_cast<u32x4_t*>(dst + 128 * k) = u32x4_t{dq_w[0], dq_w[1], dq_w[2], dq_w[3]};
-        F[k] = *reinterpret_cast<const u32x2_t*>(src + 64 * k);
-      }
+    }
+    {
+      static_assert(STEPS / CONV_EVERY == UPL, "the last unit ends with the loop");
+      constexpr int k = UPL - 1;
+      *reinterpret_cast<u32x4_t*>(dst + 128 * k) = u32x4_t{dq_w[0], dq_w[1], dq_w[2], dq_w[3]};
+      F[k] = *reinterpret_cast<const u32x2_t*>(src + 64 * k);
     }
   };
 
