@@ -803,9 +803,8 @@ void partial_latent_fp8_kernel(const PartialArgs a) {
         if (st + KP < KS) kf[(st + KP) % (KP + 1)] = kread(st + KP);
         qk_step(st, kf[st % (KP + 1)], qf[st], s);
         // the previous unit's LDS store and the next fetch into its
-        // registers, one product after the unit's last operation, so that
-        // the store does not wait on it (the next unit writes dq_w only in
-        // its second step)
+        // registers come one product after that unit's last operation (in
+        // the step before), so that the store does not wait on its result
         if (st % CONV_EVERY == 0 && st > 0 && st / CONV_EVERY - 1 < UPL) {
           const int k = st / CONV_EVERY - 1;
           *reinterpret_cast<u32x4_t*>(dst + 128 * k) = u32x4_t{dq_w[0], dq_w[1], dq_w[2], dq_w[3]};
