@@ -588,7 +588,45 @@ void partial_latent_fp8_kernel(const PartialArgs a) {
   // Q^T fragments: lane -> row n32, dims 16ks + 8hf + 0..7. Issued before
   // the page-table reads below, which their issue then overlaps.
   u32x4_t qf[KS];
-  {
+  if (!stacked && a.Hkv == 1) {
+    // One latent KV head: the view's rows are consecutive rows of q (row r
+    // of request b is q row b T Hq + r). Each wave reads its 32 rows in
+    // thirds of the dims with loads whose lanes cover consecutive 16-byte
+    // chunks of a row (a few cache lines per load instead of 32), stages
+    // them in its own part of tile buffers 1-2 (free until the tile loop;
+    // rows padded to 400 bytes, so the fragment reads of 32 rows hit
+    // distinct banks) and reads its fragments back. Rows past the view
+    // repeat its last row and are zeroed.
+    constexpr int QSTR = 400, NQL = RW * 24 / 64;  // row stride; 16-byte loads per lane and third
+    static_assert(DK == 576 && (RW * 24) % 64 == 0, "thirds of 192 dims, whole loads");
+    static_assert(NW * RW * QSTR <= 2 * (int)sizeof(sbuf[0]), "staging fits buffers 1-2");
+    const char* q0 = reinterpret_cast<const char*>(a.q) +
+                     ((size_t)b * a.q_tokens * a.Hq) * RB;
+    char* stage = reinterpret_cast<char*>(sbuf) + sizeof(sbuf[0]) + wave * (RW * QSTR);
+    const bool live = my_row < nrows;
+#pragma unroll
+    for (int p3 = 0; p3 < 3; ++p3) {
+      u32x4_t raw[NQL];
+#pragma unroll
+      for (int i = 0; i < NQL; ++i) {
+        const int c = 64 * i + lane, rr = c / 24, cq = c % 24;
+        const int row = min(row0 + RW * wave + rr, nrows - 1);
+        raw[i] = *reinterpret_cast<const u32x4_t*>(q0 + (size_t)row * RB + 384 * p3 + 16 * cq);
+      }
+#pragma unroll
+      for (int i = 0; i < NQL; ++i) {
+        const int c = 64 * i + lane, rr = c / 24, cq = c % 24;
+        *reinterpret_cast<u32x4_t*>(stage + rr * QSTR + 16 * cq) = raw[i];
+      }
+      // a wave's LDS operations complete in order: these reads see the
+      // stores above, and the next third's stores follow them
+#pragma unroll
+      for (int k = 0; k < 12; ++k) {
+        const u32x4_t x = *reinterpret_cast<const u32x4_t*>(stage + n32 * QSTR + 16 * (2 * k + hf));
+        qf[12 * p3 + k] = live ? x : u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+  } else {
     int qb = b, head = 0;
     const bool live = my_row < nrows;
     if (live) {
