@@ -748,6 +748,36 @@ void partial_latent_fp8_kernel(const PartialArgs a) {
     }
   };
 
+  // V^T fragment i = DB kk + db (32 dims x 16 tokens) of the tile at tv,
+  // from the lane's offset v0 (see above)
+  auto vread_from = [&](const char* tv, int v0, int i) {
+    const int kk = i / DB, db = i % DB;
+    const char* p0 = tv + (v0 ^ (64 * (db & 1))) + 128 * (db >> 1) + 16 * kk * RB;
+    const char* p1 = tv + (v0 ^ (64 * (db & 1) + 32)) + 128 * (db >> 1) + (16 * kk + 8) * RB;
+    const u32x2_t x0 = __builtin_bit_cast(
+        u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p0));
+    const u32x2_t x1 = __builtin_bit_cast(
+        u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p1));
+    return u32x4_t{x0[0], x0[1], x1[0], x1[1]};
+  };
+
+  // The O^T products of the last tile alone, after the tile loop: no S^T
+  // product or dequantization is left to pair them with.
+  auto pv_tail = [&](const uint16_t* prev, const bf16x8_t (&pb)[2]) {
+    constexpr int VP = 2, NPV = 2 * DB;
+    const char* tv = reinterpret_cast<const char*>(prev);
+    int v0;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(v0) : "v"(vofs));
+    u32x4_t vf[VP + 1];
+#pragma unroll
+    for (int q = 0; q < VP; ++q) vf[q] = vread_from(tv, v0, q);
+#pragma unroll
+    for (int st = 0; st < NPV; ++st) {
+      if (st + VP < NPV) vf[(st + VP) % (VP + 1)] = vread_from(tv, v0, st + VP);
+      pv_step(st, vf[st % (VP + 1)], pb[st / DB], acc[st % DB]);
+    }
+  };
+
   // One interval's products: S^T of tile `cur` (a chain of KS dependent
   // MFMAs) interleaved with O^T += V^T . P^T of the tile before it (2 DB
   // MFMAs on DB independent accumulators, k-step major), which spreads the
@@ -771,16 +801,7 @@ void partial_latent_fp8_kernel(const PartialArgs a) {
     auto kread = [&](int ks) {
       return *reinterpret_cast<const u32x4_t*>(tk + (k0 ^ (32 * (ks & 3))) + 128 * (ks >> 2));
     };
-    auto vread = [&](int i) {  // i = DB kk + db
-      const int kk = i / DB, db = i % DB;
-      const char* p0 = tv + (v0 ^ (64 * (db & 1))) + 128 * (db >> 1) + 16 * kk * RB;
-      const char* p1 = tv + (v0 ^ (64 * (db & 1) + 32)) + 128 * (db >> 1) + (16 * kk + 8) * RB;
-      const u32x2_t x0 = __builtin_bit_cast(
-          u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p0));
-      const u32x2_t x1 = __builtin_bit_cast(
-          u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p1));
-      return u32x4_t{x0[0], x0[1], x1[0], x1[1]};
-    };
+    auto vread = [&](int i) { return vread_from(tv, v0, i); };  // i = DB kk + db
     // the tile after next (page uniform over the tile)
     const int pid = __builtin_amdgcn_readfirstlane(sm_pid[(t_fetch >> shift) - pg_first]);
     const char* src = kbase + pid * kb_stride + (long long)(t_fetch & pmask) * DK +
@@ -931,25 +952,27 @@ void partial_latent_fp8_kernel(const PartialArgs a) {
     bf16x8_t pb[2] = {};
     // interval i: tile i + 1 dequantized into buffer (i + 1) % 3 (and tile
     // i + 2 fetched), S^T of tile i from buffer i % 3 with O^T of tile
-    // i - 1 from buffer (i + 2) % 3, then the softmax of tile i
+    // i - 1 from buffer (i + 2) % 3, then the softmax of tile i; the O^T
+    // products of the last tile follow the loop alone.
     // Every interval runs the same products (one code path keeps the
     // registers the allocator needs to the products'): before the first
     // tile the O^T product reads tile 0 with P = 0 (it adds exact zeros);
-    // past the last tile the S^T product reruns the last tile and its
-    // scores are dropped. Waves whose rows are all padding compute with
-    // zero queries and write nothing.
-    for (int i = 0, bi = 0; i <= n_tt && !restart; ++i, bi = (bi == 2) ? 0 : bi + 1) {
+    // the last interval dequantizes a repeat of the last tile into an
+    // unused buffer. Waves whose rows are all padding compute with zero
+    // queries and write nothing.
+    for (int i = 0, bi = 0; i < n_tt && !restart; ++i, bi = (bi == 2) ? 0 : bi + 1) {
       const int bp = bi == 0 ? 2 : bi - 1;
-      const uint16_t* cur = sbuf[i < n_tt ? bi : bp];
+      const uint16_t* cur = sbuf[bi];
       const uint16_t* prev = sbuf[i > 0 ? bp : bi];
       uint16_t* next = sbuf[bi == 2 ? 0 : bi + 1];
       const int t_fetch = min(start + (i + 2) * kTT, t_last);
       f32x16_t s;
       products(cur, prev, pb, s, next, F, t_fetch);
-      if (live_wave && i < n_tt) softmax(s, start + i * kTT, pass, pb);
+      if (live_wave) softmax(s, start + i * kTT, pass, pb);
       lds_barrier();  // tiles i - 1 and i read by all waves; tile i + 1 staged
       restart = sm_restart > pass;  // uniform over the workgroup
     }
+    if (!restart && n_tt > 0) pv_tail(sbuf[(n_tt - 1) % 3], pb);
     if (!restart) break;
   }
   // the last products' results before any VALU reads them
