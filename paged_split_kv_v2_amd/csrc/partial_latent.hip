@@ -493,16 +493,16 @@ void partial_latent_kernel(const PartialArgs a) {
 // product's accumulator the same register file and has no room for both.
 // The query fragments are fetched first, so that their issue (36 loads of
 // 32 rows each) overlaps the page-table reads.
-// Measured (32 requests x 16384 fp8 tokens, 2048-token partitions): about
-// 170 us per launch against 195 us for the 8-wave kernel above; with the
-// matrix cores 36% busy by counter, LDS 23% busy, no bank conflicts. Cycle
-// stamps (s_memtime) per workgroup: prologue 8 us, tile loop 134 us, the
-// partial's stores 14 us; the clock under this load is 1.8-2.0 GHz, not
-// 2.4. An interval takes about 4,100 cycles against 2,176 of products:
-// the softmax (about 560 cycles) runs with the matrix core idle, and the
-// LDS stores of the dequantized tile and the vector operations cost about
-// 450 and 300 cycles of the products loop. With one wave per SIMD no other
-// wave fills the issue slots they take.
+// Measured (32 requests x 16384 fp8 tokens, 2048-token partitions): 160-166
+// us per launch against 195 us for the 8-wave kernel above; with the
+// matrix cores 40% busy by counter, LDS 26% busy, no bank conflicts. Cycle
+// stamps (s_memtime) per workgroup: prologue about 7 us, tile loop about
+// 130 us, the partial's stores 12 us; the clock under this load is 1.8-2.0
+// GHz, not 2.4. An interval takes about 4,000 cycles against 2,176 of
+// products: the launch is bound by the one wave's instruction issue (about
+// 430 other instructions per interval: the dequantization, the softmax,
+// LDS reads and waits), and with one wave per SIMD no other wave fills
+// the issue slots they take.
 // Softmax reference: a row's scores are exponentiated against a fixed
 // reference, its maximum over the first tile it sees, and the accumulators
 // are never rescaled (a VALU rescale of accumulator registers costs the
