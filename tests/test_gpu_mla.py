@@ -158,3 +158,39 @@ def test_mla_scores_far_above_the_first_tile(gpu):
     assert np.all(s > 10), s
     assert_close(out, fo, TOL["fp8_e4m3"], "out")
     assert_lse(lse, fl, "lse")
+
+
+@pytest.mark.parametrize("Hq", [128, 80])
+def test_latent_fp8_shared_prefix_stacked(gpu, Hq):
+    """A shared-prefix cascade over an fp8 latent pool [cascade-PR, "The
+    decomposition"]: the shared span's level-0 launch stacks three members'
+    query rows (three row tiles at 128 heads), so the fp8 latent kernel takes
+    each wave's query rows from one member's slot; at 80 heads a wave's rows
+    straddle two members. Against the one-softmax definition per request."""
+    from oracle import attention as oatt
+    lens = [700, 450, 520, 300]
+    b = W.random_batch(3131, batch=4, page_size=64, num_q_heads=Hq, num_kv_heads=1,
+                       head_dim=576, head_dim_v=512, kv_dtype="fp8_e4m3", q_dtype="bf16",
+                       min_len=0, max_len=0, partition_tokens=256, lens=lens,
+                       share=[([0, 1, 2], 6)], latent=True)
+    pool, _, q = to_device(b)
+    plan = gpu.CascadePlan(b.indptr, b.indices, b.kv_len, 64,
+                           gpu.CascadeParams(enabled=1, min_shared_pages=2,
+                                             l0_partition_tokens=256, l1_partition_tokens=256))
+    out, lse = plan.run(pool, q, b.sm_scale)
+    torch.cuda.synchronize()
+    assert plan.stats()[0]["members"] == 3
+    ro, rl = oatt.decode_attention(b)
+    assert_close(out.cpu().numpy(), ro, TOL["fp8_e4m3"], "out")
+    assert_lse(lse.cpu().numpy(), rl, "lse")
+
+
+def test_latent_fp8_80_query_heads(gpu):
+    """80 query heads on one latent KV head: the third wave of a workgroup
+    holds 16 live rows and the fourth none. Partials and flat decode against
+    the oracle."""
+    from test_gpu_partial import check_partials_and_flat
+    b = W.random_batch(3132, batch=3, page_size=64, num_q_heads=80, num_kv_heads=1,
+                       head_dim=576, head_dim_v=512, kv_dtype="fp8_e4m3", q_dtype="bf16",
+                       min_len=1, max_len=700, partition_tokens=256, latent=True)
+    check_partials_and_flat(gpu, b)
