@@ -142,7 +142,11 @@ int pdk_stacked_head_map(int32_t num_members, int32_t num_kv_heads, int32_t grou
  * Dtypes: q f32|bf16; pool f32|bf16|fp8_e4m3 (fp8 is dequantized to bf16
  * with the pool's scale on load [DCP-PR, 3.2 figure, 3.3]).
  * Errors: PDK_ERR_ARG, PDK_ERR_SHAPE, PDK_ERR_DTYPE, PDK_ERR_UNSUPPORTED
- * (head dims / head counts without an instantiated kernel), PDK_ERR_HIP. */
+ * (head dims / head counts without an instantiated kernel, or a partition of
+ * more pages than the chosen kernel stages: partition_tokens / page_size at
+ * most 1023 on the vector path and the head-dim-128 matrix-core path on
+ * 1-2 token pages, 511 on the LDS-ring path (>= 16 rows per KV head, pages
+ * of >= 4 tokens), 255 on the latent 576/512 paths), PDK_ERR_HIP. */
 int pdk_paged_decode_partial(const pdk_kv_pool* pool, const pdk_csr* csr_dev, const void* q,
                              int32_t q_dtype, int32_t num_q_heads, float sm_scale,
                              int32_t partition_tokens, const int32_t* part_indptr_dev,

@@ -128,3 +128,27 @@ def test_page_table_checks_name_the_violation():
         assert lib().pdk_last_error()
     c, keep = host_csr([[0, 1, 2], [3]], [40, 10])
     assert lib().pdk_validate_csr(ctypes.byref(c), 16, 8) == 0
+
+
+ERR_UNSUPPORTED = -4
+FP8 = 2  # pdk_dtype (PDK_FP8_E4M3)
+
+
+@pytest.mark.parametrize("P,Hkv,Hq,D,Dv,dtype,limit", [
+    (16, 8, 32, 128, 128, BF16, 1023),   # vector path (4 rows per KV head)
+    (16, 2, 32, 128, 128, BF16, 511),    # LDS-ring path (16 rows per KV head)
+    (2, 1, 32, 128, 128, BF16, 1023),    # matrix-core path on 2-token pages (32 rows)
+    (64, 1, 128, 576, 512, FP8, 255),    # latent fp8 path (128 rows)
+])
+def test_partition_spanning_too_many_pages_is_unsupported(P, Hkv, Hq, D, Dv, dtype, limit):
+    """Each partial kernel stages a partition's page ids in LDS, so a
+    partition of more pages than its table holds is refused on the host with
+    PDK_ERR_UNSUPPORTED (one page over the limit that
+    pdk_paged_decode_partial documents for the path)."""
+    p = pdk._Pool(k=FAKE, v=None if Dv != D else FAKE, num_blocks=4096, page_size=P,
+                  num_kv_heads=Hkv, head_dim_k=D, head_dim_v=Dv, dtype=dtype, k_scale=0.01,
+                  v_scale=0.01)
+    c = dev_csr()
+    rc = lib().pdk_paged_decode_partial(ctypes.byref(p), ctypes.byref(c), FAKE, BF16, Hq, 0.125,
+                                        (limit + 1) * P, FAKE, 4, FAKE, FAKE, None)
+    status(rc, ERR_UNSUPPORTED, f"more than {limit} pages")

@@ -125,3 +125,22 @@ def test_stacked_rows_page_sizes(gpu, page_size):
                        num_kv_heads=2, head_dim=128, kv_dtype="bf16", q_dtype="bf16",
                        min_len=0, max_len=0, partition_tokens=S, lens=lens)
     check_partials_and_flat(gpu, b)
+
+
+@pytest.mark.parametrize("P,Hkv,Hq,D,Dv,kv,pages", [
+    (16, 8, 32, 128, 128, "bf16", 1023),       # vector path
+    (16, 2, 32, 128, 128, "bf16", 511),        # LDS-ring path
+    (2, 1, 32, 128, 128, "bf16", 1023),        # matrix-core path, 2-token pages
+    (64, 1, 128, 576, 512, "fp8_e4m3", 255),   # latent fp8 path
+])
+def test_largest_partition_each_path_accepts(gpu, P, Hkv, Hq, D, Dv, kv, pages):
+    """Partitions of the most pages each kernel stages (one more is refused on
+    the host): a request of two such partitions and a ragged tail, one of
+    exactly one, one shorter than a page. Partials and flat decode against
+    the oracle."""
+    S = pages * P
+    lens = [2 * S + 37, S, 1]
+    b = W.random_batch(4100 + P, batch=3, page_size=P, num_q_heads=Hq, num_kv_heads=Hkv,
+                       head_dim=D, head_dim_v=Dv, kv_dtype=kv, q_dtype="bf16", min_len=0,
+                       max_len=0, partition_tokens=S, lens=lens, latent=Dv != D)
+    check_partials_and_flat(gpu, b)
