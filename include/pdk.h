@@ -516,6 +516,30 @@ int pdk_run_chunked_multi_token(const pdk_chunked_plan* plan, const pdk_kv_pool*
                                 float* out, float* lse_out, float* chunk_out, float* chunk_lse,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Step graphs: the kernel launches of one decode step recorded once by HIP
+ * stream capture and replayed with one launch (a decode loop then makes one
+ * host call per step). Between pdk_graph_begin(stream) and
+ * pdk_graph_end(stream, &g) the caller makes run calls on `stream` only:
+ * pdk_run_cascade_decode / _partials / _merge, pdk_run_chunked_decode /
+ * _multi_token, pdk_decode_flat, pdk_paged_decode_partial, pdk_merge_states
+ * (each only launches kernels). Plans must be uploaded, workspaces and
+ * outputs allocated beforehand: nothing may allocate, copy from the host or
+ * synchronize while recording, and stream must not be the null stream. A
+ * replay (pdk_graph_launch, any stream) runs the recorded kernels with the
+ * recorded arguments: it reads the current contents of every buffer the
+ * calls named (queries, pools, device page tables, uploaded plans) and
+ * writes the same outputs, so a plan may not be re-uploaded elsewhere or
+ * freed while its graph lives. pdk_graph_end always ends the capture; on a
+ * capture error it returns PDK_ERR_HIP and no graph. pdk_graph_nodes counts
+ * the recorded kernel nodes and any other nodes (none for the calls above).
+ * The graph is owned by the caller: pdk_graph_free. */
+typedef struct pdk_graph pdk_graph;
+int pdk_graph_begin(hipStream_t stream);
+int pdk_graph_end(hipStream_t stream, pdk_graph** out);
+int pdk_graph_launch(const pdk_graph* graph, hipStream_t stream);
+int pdk_graph_nodes(const pdk_graph* graph, int32_t* kernel_nodes, int32_t* other_nodes);
+void pdk_graph_free(pdk_graph* graph);
+
 /* Thread-local description of the last non-OK status on this thread. */
 const char* pdk_last_error(void);
 

@@ -27,7 +27,7 @@ import torch
 
 __all__ = [
     "PdkError", "lib", "KVPool", "DeviceCSR", "CascadeParams", "CascadePlan", "ChunkedPlan",
-    "PlanCache", "cascade_autotune", "cascade_tuned_params", "cascade_tuning_key",
+    "PlanCache", "StepGraph", "cascade_autotune", "cascade_tuned_params", "cascade_tuning_key",
     "cascade_tuning_clear",
     "partition_indptr", "validate_csr", "parse_switch", "cascade_enabled_from_env",
     "stacked_head_map", "paged_decode_partial", "merge_states", "decode_flat",
@@ -126,6 +126,11 @@ _SIGS = {
                                   _P]),
     "pdk_run_chunked_multi_token": (_I, [_P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _P, _P, _P, _S,
                                          _P]),
+    "pdk_graph_begin": (_I, [_P]),
+    "pdk_graph_end": (_I, [_P, _P]),
+    "pdk_graph_launch": (_I, [_P, _P]),
+    "pdk_graph_nodes": (_I, [_P, _P, _P]),
+    "pdk_graph_free": (None, [_P]),
     "pdk_last_error": (ctypes.c_char_p, []),
 }
 
@@ -774,3 +779,50 @@ class ChunkedPlan:
                                                 _ptr(chunk_lse), _ptr(self.workspace),
                                                 int(self.workspace.numel()), _stream(stream)))
         return out, lse_out
+
+
+# --------------------------------------------------------------------------
+# Step graphs
+# --------------------------------------------------------------------------
+
+class StepGraph:
+    """The kernel launches that ``fn()`` makes through the library, recorded
+    once by HIP stream capture (on a side stream) and replayed with one
+    launch per ``replay()``. ``fn`` must only make run calls with every plan
+    uploaded and every output and workspace allocated: nothing may allocate,
+    copy from the host or synchronize while it records. A replay reads the
+    current contents of the buffers the calls named and writes the same
+    outputs; the objects those calls used (plans, pools, tensors) must stay
+    alive as long as the graph."""
+
+    def __init__(self, fn, keep=()):
+        cur = torch.cuda.current_stream()
+        side = torch.cuda.Stream(device=cur.device)
+        side.wait_stream(cur)
+        h = ctypes.c_void_p()
+        with torch.cuda.stream(side):
+            _check(lib().pdk_graph_begin(_stream(side)))
+            try:
+                fn()
+            except BaseException:
+                if lib().pdk_graph_end(_stream(side), ctypes.byref(h)) == 0:
+                    lib().pdk_graph_free(h)
+                raise
+            _check(lib().pdk_graph_end(_stream(side), ctypes.byref(h)))
+        cur.wait_stream(side)
+        self._h = h
+        self._keep = (fn, side, *keep)
+
+    def replay(self, stream=None):
+        _check(lib().pdk_graph_launch(self._h, _stream(stream)))
+
+    def node_counts(self):
+        """(kernel nodes, other nodes) recorded."""
+        k, o = ctypes.c_int32(), ctypes.c_int32()
+        _check(lib().pdk_graph_nodes(self._h, ctypes.byref(k), ctypes.byref(o)))
+        return k.value, o.value
+
+    def __del__(self):
+        if getattr(self, "_h", None) and _lib is not None:
+            _lib.pdk_graph_free(self._h)
+            self._h = None

@@ -152,3 +152,14 @@ def test_partition_spanning_too_many_pages_is_unsupported(P, Hkv, Hq, D, Dv, dty
     rc = lib().pdk_paged_decode_partial(ctypes.byref(p), ctypes.byref(c), FAKE, BF16, Hq, 0.125,
                                         (limit + 1) * P, FAKE, 4, FAKE, FAKE, None)
     status(rc, ERR_UNSUPPORTED, f"more than {limit} pages")
+
+
+def test_step_graph_calls_check_their_arguments():
+    """Capture needs a stream other than the null stream; a NULL graph is
+    refused by launch and by the node count; freeing NULL is a no-op."""
+    status(lib().pdk_graph_begin(None), ERR_ARG, "null stream")
+    status(lib().pdk_graph_end(None, None), ERR_ARG, "null stream")
+    status(lib().pdk_graph_launch(None, None), ERR_ARG, "null graph")
+    k, o = ctypes.c_int32(), ctypes.c_int32()
+    status(lib().pdk_graph_nodes(None, ctypes.byref(k), ctypes.byref(o)), ERR_ARG, "null")
+    lib().pdk_graph_free(None)
