@@ -144,3 +144,41 @@ def test_largest_partition_each_path_accepts(gpu, P, Hkv, Hq, D, Dv, kv, pages):
                        head_dim=D, head_dim_v=Dv, kv_dtype=kv, q_dtype="bf16", min_len=0,
                        max_len=0, partition_tokens=S, lens=lens, latent=Dv != D)
     check_partials_and_flat(gpu, b)
+
+
+@pytest.mark.parametrize("P,Hkv,Hq,D,Dv,kv,base", [
+    (16, 8, 32, 128, 128, "bf16", 140_000),        # vector path, 32 KiB pool rows
+    (16, 2, 32, 128, 128, "bf16", 600_000),        # LDS-ring path, 8 KiB rows
+    (2, 1, 32, 128, 128, "bf16", 9_000_000),       # matrix-core path, 512 B rows
+    (64, 1, 128, 576, 512, "fp8_e4m3", 120_000),   # latent fp8 path, 36 KiB rows
+])
+def test_page_ids_past_4gib_of_pool(gpu, P, Hkv, Hq, D, Dv, kv, base):
+    """Every page a request reads lies more than 4 GiB (and more than 2^31
+    elements) into its pool: the same rows as a small pool, moved up by
+    `base` rows of a large one, with the page ids moved by the same amount.
+    Partials and flat decode against the oracle on the small pool."""
+    b = W.random_batch(4200 + P, batch=3, page_size=P, num_q_heads=Hq, num_kv_heads=Hkv,
+                       head_dim=D, head_dim_v=Dv, kv_dtype=kv, q_dtype="bf16", min_len=1,
+                       max_len=900, partition_tokens=256, latent=Dv != D)
+    small, _, q = to_device(b)
+
+    def lift(t):
+        big = torch.empty((base + t.shape[0],) + tuple(t.shape[1:]), dtype=t.dtype,
+                          device=t.device)
+        big[base:] = t
+        return big
+
+    pool = gpu.KVPool(k=lift(small.k), v=None if small.v is None else lift(small.v),
+                      head_dim_v=small.head_dim_v, k_scale=small.k_scale, v_scale=small.v_scale)
+    assert pool.k.numel() * pool.k.element_size() > 4 << 30
+    assert base * pool.k[0].numel() > 2**31
+    csr = gpu.DeviceCSR.from_host(b.indptr, b.indices + base, b.kv_len)
+    v, l, pind = partials(gpu, b, pool, csr, q)
+    rv, rl, _ = oatt.partial_attention(b)
+    tol = TOL[b.kv_dtype]
+    assert_close(v, rv, tol, "partial out")
+    assert_lse(l, rl, "partial lse")
+    out, lse, _ = flat_decode(b, pool, csr, q)
+    ro, rlse = oatt.decode_attention(b)
+    assert_close(out.cpu().numpy(), ro, tol, "flat out")
+    assert_lse(lse.cpu().numpy(), rlse, "flat lse")
