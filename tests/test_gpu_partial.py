@@ -182,3 +182,15 @@ def test_page_ids_past_4gib_of_pool(gpu, P, Hkv, Hq, D, Dv, kv, base):
     ro, rlse = oatt.decode_attention(b)
     assert_close(out.cpu().numpy(), ro, tol, "flat out")
     assert_lse(lse.cpu().numpy(), rlse, "flat lse")
+
+
+def test_many_short_requests(gpu):
+    """2,000 requests of 0-70 tokens (empty ones included) in 32-token
+    partitions: the request search over a long batch, many partitions and
+    merge groups of every small size. Partials and flat decode against the
+    oracle."""
+    b = W.random_batch(4300, batch=2000, page_size=16, num_q_heads=32, num_kv_heads=8,
+                       head_dim=128, kv_dtype="bf16", q_dtype="bf16", min_len=0, max_len=70,
+                       partition_tokens=32)
+    assert (b.kv_len == 0).any() and b.kv_len.max() > 64
+    check_partials_and_flat(gpu, b)
