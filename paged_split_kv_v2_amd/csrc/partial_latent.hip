@@ -7,8 +7,10 @@
 // contract as the other partial kernels: one normalized partial and its log2
 // LSE per (request, partition, query row).
 //
-// Workgroup = 8 waves (two per SIMD), 128 query rows; wave w owns rows
-// [16w, 16w+16) for the whole partition:
+// Workgroup = 8 waves (two per SIMD), 128 query rows, or 4 waves and 64
+// rows for launches whose 128-row grid would not cover the CUs (a short new-
+// token range split into few partitions); wave w owns rows [16w, 16w+16)
+// for the whole partition:
 //   * Q^T as B operands of v_mfma_f32_16x16x32_bf16 (18 k-steps x 8 bf16 per
 //     lane) and O^T = 512 dims x 16 rows as 32 accumulator blocks of 16x16
 //     (128 registers per lane); no exchange between waves;
@@ -26,7 +28,8 @@
 //     lane group q are the tokens {4q..4q+3} and {16+4q..16+4q+3}, and the V^T
 //     loads use the same token order);
 //   * online softmax per query row in log2 units, lazy reference maximum as
-//     in the other kernels; P is rounded to bf16 for the PV product.
+//     in the other kernels; P enters the PV product as bf16 hi + lo parts
+//     (two products per block).
 // Pipeline: three bf16 tile buffers and one raw staging buffer. While tile i
 // is multiplied from one buffer, tile i + 1 (fetched during tile i - 1 by
 // gfx950's global->LDS loads, 16 bytes per lane at base + 16*lane) is
@@ -57,9 +60,8 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 enum { LK_BF16 = 1, LK_FP8 = 2 };
 constexpr int kTT = 32;          // tokens per tile
-constexpr int kWaves = 8;
-constexpr int kRows = 128;
 constexpr int kMaxPagesL = 256;  // pages of one partition (plus one)
+constexpr int kChipCUs = 256;    // compute units of an MI355X
 constexpr float kLazyL = 8.f;
 constexpr bool kStagger = true;  // second half of the waves one PV product behind
 
@@ -81,9 +83,10 @@ __device__ __forceinline__ void lds_barrier() {
 // Instruction classes of __builtin_amdgcn_sched_group_barrier.
 enum : int { SG_MFMA = 0x008, SG_DS_READ = 0x100 };
 
-template <int DK, int DV, int KT>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int DK, int DV, int KT, int kWaves>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 void partial_latent_kernel(const PartialArgs a) {
+  constexpr int kRows = 16 * kWaves;  // query rows per workgroup
   constexpr int NT = 64 * kWaves;
   constexpr int KS = DK / 32;                       // k-steps of S^T (32 dims)
   constexpr int DB = DV / 16;                       // 16-dim output blocks
@@ -302,8 +305,10 @@ void partial_latent_kernel(const PartialArgs a) {
 
   // online softmax of one tile's scores: rescales the running state and
   // returns P^T as the B operand of the PV product (k slots 8q4 + i are
-  // tokens 4q4 + i (i < 4) and 16 + 4q4 + i - 4)
-  auto softmax = [&](f32x4_t (&s)[2], int t0) {
+  // tokens 4q4 + i (i < 4) and 16 + 4q4 + i - 4), split into bf16 hi + lo
+  // parts (lo = P - hi, rounded) so that the product keeps P to about 16
+  // bits (one bf16 rounding of P alone errs by up to 2^-9 per weight)
+  auto softmax = [&](f32x4_t (&s)[2], int t0, bf16x8_t& plo) {
     // row max over the four lane groups, in scaled log2 units; a full tile
     // scales inside the exponent below, the last tile masks first
     float cs = a.scale_log2, mx;
@@ -342,7 +347,7 @@ void partial_latent_kernel(const PartialArgs a) {
       run_m = mn;
     }
     const float mu = (run_m == -INFINITY) ? 0.f : run_m;
-    uint32_t pw[4];
+    uint32_t pw[4], pl[4];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
@@ -350,14 +355,17 @@ void partial_latent_kernel(const PartialArgs a) {
         const float p0 = fast_exp2(__builtin_fmaf(s[tb][j], cs, -mu));
         const float p1 = fast_exp2(__builtin_fmaf(s[tb][j + 1], cs, -mu));
         run_l += p0 + p1;
-        pw[2 * tb + (j >> 1)] = pack_bf16x2_rne(p0, p1);
+        const uint32_t hw = pack_bf16x2_rne(p0, p1);
+        pw[2 * tb + (j >> 1)] = hw;
+        pl[2 * tb + (j >> 1)] = pack_bf16x2_rne(p0 - bf16_lo(hw), p1 - bf16_hi(hw));
       }
+    plo = as_bf16x8(u32x4_t{pl[0], pl[1], pl[2], pl[3]});
     return as_bf16x8(u32x4_t{pw[0], pw[1], pw[2], pw[3]});
   };
 
   // O^T += V^T . P^T, V^T fragments by transposing loads issued VP products
   // ahead
-  auto pv_phase = [&](const uint16_t* tile_k, bf16x8_t pb) {
+  auto pv_phase = [&](const uint16_t* tile_k, bf16x8_t pb, bf16x8_t plo) {
     constexpr int VP = 2;
     u32x4_t vf[DB];
     int v0;
@@ -375,14 +383,15 @@ void partial_latent_kernel(const PartialArgs a) {
     for (int db = 0; db < DB; ++db) {
       if (db + VP < DB) vf[db + VP] = vread(db + VP);
       acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vf[db]), pb, acc[db], 0, 0, 0);
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vf[db]), plo, acc[db], 0, 0, 0);
     }
     __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2 * VP, 0);
 #pragma unroll
     for (int i = 0; i < DB - VP; ++i) {
       __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(SG_MFMA, VP, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2 * VP, 0);
   };
 
   // Interval i (one barrier each): tile i is read from buffer i % 3; tile
@@ -395,7 +404,7 @@ void partial_latent_kernel(const PartialArgs a) {
   // conversion then fall beside the other's products. Buffer (i - 1) % 3
   // stays intact until interval i + 1 converts into it.
   const bool lagged = kStagger && wave >= kWaves / 2;  // wave-uniform
-  bf16x8_t pb{};  // P^T of the last tile (lagged waves: not yet applied)
+  bf16x8_t pb{}, plo{};  // P^T of the last tile (lagged waves: not yet applied)
   auto interval = [&](int i, const uint16_t* cur, uint16_t* next, const uint16_t* prev) {
     const int t0 = start + i * kTT;
     auto convert_next = [&]() {
@@ -406,15 +415,15 @@ void partial_latent_kernel(const PartialArgs a) {
     };
     if (lagged) {
       convert_next();
-      if (i > 0) pv_phase(prev, pb);
+      if (i > 0) pv_phase(prev, pb, plo);
     }
     f32x4_t s[2];
     s_phase(cur, s);
     if (lagged && i + 2 < n_tt) fetch_tile(t0 + 2 * kTT);
-    pb = softmax(s, t0);
+    pb = softmax(s, t0, plo);
     if (!lagged) {
       convert_next();
-      pv_phase(cur, pb);
+      pv_phase(cur, pb, plo);
       if (i + 2 < n_tt) fetch_tile(t0 + 2 * kTT);
     }
     lds_barrier();  // tile i read by all waves; tile i + 1 staged
@@ -426,7 +435,7 @@ void partial_latent_kernel(const PartialArgs a) {
   }
   if (lagged && n_tt > 0) {  // no fetch in flight here
     const int last = (n_tt - 1) % 3;
-    pv_phase(last == 0 ? sk0 : last == 1 ? sk1 : sk2, pb);
+    pv_phase(last == 0 ? sk0 : last == 1 ? sk1 : sk2, pb, plo);
   }
 
   // row sum over the lane groups, normalized partial and its LSE
@@ -1014,20 +1023,32 @@ int launch_partial_latent(const PartialArgs& a, hipStream_t stream, bool* handle
       a.max_rows < 64 || a.p_shift < 0 || a.P % kTT != 0)
     return PDK_OK;
   const bool fp8 = a.kv_dtype == PDK_FP8_E4M3;
-  LatentFn fn = fp8 ? partial_latent_fp8_kernel<576, 512>
-              : a.kv_dtype == PDK_BF16 ? partial_latent_kernel<576, 512, LK_BF16>
-                                       : nullptr;
-  if (!fn) return PDK_OK;
+  if (!fp8 && a.kv_dtype != PDK_BF16) return PDK_OK;
   if (a.S / a.P + 1 > kMaxPagesL)
     return fail(PDK_ERR_UNSUPPORTED, "partition of %d tokens spans more than %d pages", a.S,
                 kMaxPagesL - 1);
   *handled = true;
-  const int n_tiles = (a.max_rows + kRows - 1) / kRows;  // both kernels: 128 rows per workgroup
   const long long units = (long long)a.num_parts * a.Hkv;
+  // Rows per workgroup: 128 (the fp8 kernel always; the bf16 kernel's 8
+  // waves). A bf16 launch whose 128-row grid would leave CUs idle (a short
+  // suffix range: few partitions) takes 64-row workgroups of 4 waves
+  // instead, twice the workgroups for the same rows, and so does one of at
+  // most 64 rows (no dead waves).
+  int rows = 128, threads = 256;
+  LatentFn fn = partial_latent_fp8_kernel<576, 512>;
+  if (!fp8) {
+    const long long blocks128 = xcd_grid_blocks(units, (a.max_rows + 127) / 128);
+    const bool narrow = a.max_rows <= 64 || blocks128 < kChipCUs;
+    rows = narrow ? 64 : 128;
+    threads = narrow ? 256 : 512;
+    fn = narrow ? partial_latent_kernel<576, 512, LK_BF16, 4>
+                : partial_latent_kernel<576, 512, LK_BF16, 8>;
+  }
+  const int n_tiles = (a.max_rows + rows - 1) / rows;
   const long long blocks = xcd_grid_blocks(units, n_tiles);
   if (blocks == 0) return PDK_OK;
   if (blocks > 0x7FFFFFFFLL) return fail(PDK_ERR_SHAPE, "grid too large (%lld)", blocks);
-  hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(fp8 ? 256 : 64 * kWaves), 0, stream, a);
+  hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(threads), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(PDK_ERR_HIP, "latent partial launch: %s", hipGetErrorString(err));
   return PDK_OK;

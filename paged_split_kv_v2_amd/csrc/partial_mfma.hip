@@ -409,7 +409,7 @@ int launch_partial_mfma(const PartialArgs& a, hipStream_t stream, bool* handled)
   } else if (a.Dk == 576 && a.Dv == 512 && latent && a.max_rows >= 64) {
     nw = 8;
     fn = a.kv_dtype == PDK_FP8_E4M3 ? partial_mfma_kernel<576, 512, 8, 32, MK_FP8, true, false>
-       : a.kv_dtype == PDK_BF16     ? partial_mfma_kernel<576, 512, 8, 32, MK_BF16, true, false>
+       : a.kv_dtype == PDK_BF16     ? partial_mfma_kernel<576, 512, 8, 32, MK_BF16, true, true>
                                     : nullptr;
   }
   if (!fn) return PDK_OK;

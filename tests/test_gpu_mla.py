@@ -160,17 +160,17 @@ def test_mla_scores_far_above_the_first_tile(gpu):
     assert_lse(lse, fl, "lse")
 
 
-@pytest.mark.parametrize("Hq", [128, 80])
-def test_latent_fp8_shared_prefix_stacked(gpu, Hq):
-    """A shared-prefix cascade over an fp8 latent pool [cascade-PR, "The
+@pytest.mark.parametrize("Hq,kv", [(128, "fp8_e4m3"), (80, "fp8_e4m3"), (128, "bf16")])
+def test_latent_shared_prefix_stacked(gpu, Hq, kv):
+    """A shared-prefix cascade over a latent pool [cascade-PR, "The
     decomposition"]: the shared span's level-0 launch stacks three members'
-    query rows (three row tiles at 128 heads), so the fp8 latent kernel takes
+    query rows (three row tiles at 128 heads), so the latent kernels take
     each wave's query rows from one member's slot; at 80 heads a wave's rows
     straddle two members. Against the one-softmax definition per request."""
     from oracle import attention as oatt
     lens = [700, 450, 520, 300]
     b = W.random_batch(3131, batch=4, page_size=64, num_q_heads=Hq, num_kv_heads=1,
-                       head_dim=576, head_dim_v=512, kv_dtype="fp8_e4m3", q_dtype="bf16",
+                       head_dim=576, head_dim_v=512, kv_dtype=kv, q_dtype="bf16",
                        min_len=0, max_len=0, partition_tokens=256, lens=lens,
                        share=[([0, 1, 2], 6)], latent=True)
     pool, _, q = to_device(b)
@@ -181,7 +181,7 @@ def test_latent_fp8_shared_prefix_stacked(gpu, Hq):
     torch.cuda.synchronize()
     assert plan.stats()[0]["members"] == 3
     ro, rl = oatt.decode_attention(b)
-    assert_close(out.cpu().numpy(), ro, TOL["fp8_e4m3"], "out")
+    assert_close(out.cpu().numpy(), ro, TOL[kv], "out")
     assert_lse(lse.cpu().numpy(), rl, "lse")
 
 
@@ -193,4 +193,21 @@ def test_latent_fp8_80_query_heads(gpu):
     b = W.random_batch(3132, batch=3, page_size=64, num_q_heads=80, num_kv_heads=1,
                        head_dim=576, head_dim_v=512, kv_dtype="fp8_e4m3", q_dtype="bf16",
                        min_len=1, max_len=700, partition_tokens=256, latent=True)
+    check_partials_and_flat(gpu, b)
+
+
+@pytest.mark.parametrize("P,lens", [
+    (64, [4096, 4096, 4090, 4101]),   # >= 256 partitions: 8-wave, 128-row workgroups
+    (64, [300, 129, 64, 1, 0]),       # a small grid: 4-wave, 64-row workgroups
+    (16, [300, 129, 64, 1, 0]),       # pages under 32 tokens: the 16-row matrix-core kernel
+])
+def test_latent_bf16_partials_at_the_bf16_bar(gpu, P, lens):
+    """bf16 latent pools (the MLA new-token range, or a bf16 cached prefix)
+    through each kernel that reads them, in 64-token partitions (ragged
+    last ones, an empty request): partials and flat decode against the
+    oracle at the bf16 bar, which needs P carried as bf16 hi + lo."""
+    from test_gpu_partial import check_partials_and_flat
+    b = W.random_batch(3133, batch=len(lens), page_size=P, num_q_heads=128, num_kv_heads=1,
+                       head_dim=576, head_dim_v=512, kv_dtype="bf16", q_dtype="bf16",
+                       min_len=0, max_len=0, partition_tokens=64, lens=lens, latent=True)
     check_partials_and_flat(gpu, b)
