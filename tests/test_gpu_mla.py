@@ -211,3 +211,17 @@ def test_latent_bf16_partials_at_the_bf16_bar(gpu, P, lens):
                        head_dim=576, head_dim_v=512, kv_dtype="bf16", q_dtype="bf16",
                        min_len=0, max_len=0, partition_tokens=64, lens=lens, latent=True)
     check_partials_and_flat(gpu, b)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_latent_fp8_short_partitions(gpu, seed):
+    """Many short fp8 partitions (24 requests of 1-63 tokens, one 64-token
+    partition each, 128 heads): where one or two tokens carry a row's
+    weight, the fp8 kernel's single bf16 rounding of P is least averaged
+    out. Partials and flat decode against the oracle at the fp8 bar."""
+    from test_gpu_partial import check_partials_and_flat
+    lens = [int(x) for x in np.random.default_rng(seed).integers(1, 64, size=24)]
+    b = W.random_batch(5000 + seed, batch=24, page_size=64, num_q_heads=128, num_kv_heads=1,
+                       head_dim=576, head_dim_v=512, kv_dtype="fp8_e4m3", q_dtype="bf16",
+                       min_len=0, max_len=0, partition_tokens=64, lens=lens, latent=True)
+    check_partials_and_flat(gpu, b)
