@@ -163,3 +163,18 @@ def test_step_graph_calls_check_their_arguments():
     k, o = ctypes.c_int32(), ctypes.c_int32()
     status(lib().pdk_graph_nodes(None, ctypes.byref(k), ctypes.byref(o)), ERR_ARG, "null")
     lib().pdk_graph_free(None)
+
+
+def test_an_empty_batch_is_a_no_op():
+    """Batch 0 (no partitions, no output rows) succeeds without touching any
+    buffer: the partial launch, the flat decode and the merge each return
+    PDK_OK before reading an address (all stand-ins here)."""
+    p, c = pool(), dev_csr(batch=0)
+    rc = lib().pdk_paged_decode_partial(ctypes.byref(p), ctypes.byref(c), FAKE, BF16, 4, 0.125, 32,
+                                        FAKE, 0, FAKE, FAKE, None)
+    assert rc == 0, lib().pdk_last_error()
+    rc = lib().pdk_decode_flat(ctypes.byref(p), ctypes.byref(c), FAKE, BF16, 4, 0.125, 32, FAKE,
+                               0, FAKE, FAKE, None, 0, None)
+    assert rc == 0, lib().pdk_last_error()
+    rc = lib().pdk_merge_states(FAKE, FAKE, 0, FAKE, 0, 4, 64, FAKE, FAKE, None)
+    assert rc == 0, lib().pdk_last_error()
