@@ -194,3 +194,25 @@ def test_many_short_requests(gpu):
                        partition_tokens=32)
     assert (b.kv_len == 0).any() and b.kv_len.max() > 64
     check_partials_and_flat(gpu, b)
+
+
+def test_every_request_empty(gpu):
+    """A batch whose requests all have no tokens: no partitions, no partial
+    launch; the merge alone writes out = 0 and lse = -inf for every row (the
+    oracle's empty state), through decode_flat and decode_flat_noalloc."""
+    b = W.random_batch(4400, batch=5, page_size=16, num_q_heads=32, num_kv_heads=8,
+                       head_dim=128, kv_dtype="bf16", q_dtype="bf16", min_len=0, max_len=0,
+                       partition_tokens=64, lens=[0] * 5)
+    pool, csr, q = to_device(b)
+    pind = gpu.partition_indptr(b.kv_len, 64)
+    assert int(pind[-1]) == 0
+    ro, rl = oatt.decode_attention(b)
+    assert np.all(ro == 0) and np.all(rl == -np.inf)
+    out, lse, _ = flat_decode(b, pool, csr, q, 64)
+    assert np.all(out.cpu().numpy() == 0) and np.all(lse.cpu().numpy() == -np.inf)
+    out2 = torch.full_like(out, float("nan"))
+    lse2 = torch.full_like(lse, float("nan"))
+    gpu.decode_flat_noalloc(pool, csr, q, b.sm_scale, 64, torch.from_numpy(pind).cuda(), 0, out2,
+                            lse2)
+    torch.cuda.synchronize()
+    assert np.all(out2.cpu().numpy() == 0) and np.all(lse2.cpu().numpy() == -np.inf)
