@@ -178,3 +178,18 @@ def test_an_empty_batch_is_a_no_op():
     assert rc == 0, lib().pdk_last_error()
     rc = lib().pdk_merge_states(FAKE, FAKE, 0, FAKE, 0, 4, 64, FAKE, FAKE, None)
     assert rc == 0, lib().pdk_last_error()
+
+
+@pytest.mark.parametrize("D,Dv,v,word", [
+    (96, 96, True, "no vector kernel"),          # head dim without an instance
+    (128, 64, True, "head_dim_k == head_dim_v"),  # separate V of another width, few rows
+])
+def test_head_dims_without_a_kernel_are_unsupported(D, Dv, v, word):
+    """A valid pool whose head dims no kernel is instantiated for is refused
+    with PDK_ERR_UNSUPPORTED on the host, before any launch."""
+    p = pdk._Pool(k=FAKE, v=FAKE if v else None, num_blocks=64, page_size=16, num_kv_heads=2,
+                  head_dim_k=D, head_dim_v=Dv, dtype=BF16, k_scale=1.0, v_scale=1.0)
+    c = dev_csr()
+    rc = lib().pdk_paged_decode_partial(ctypes.byref(p), ctypes.byref(c), FAKE, BF16, 4, 0.125, 32,
+                                        FAKE, 4, FAKE, FAKE, None)
+    status(rc, ERR_UNSUPPORTED, word)
